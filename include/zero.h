@@ -1,0 +1,173 @@
+/*
+ * zero.h - C ABI of the MI355X (gfx950) ZeRO-2 shard-step library, libzero.so.
+ *
+ * One data-parallel rank's ZeRO-2 optimizer step, as described on the page
+ * "ZeRO and FSDP: partitioning the optimizer states, the gradients and the
+ * parameters" (AI infra handbook), section "Implementing ZeRO's Adam from
+ * scratch" (class ZeroAdam), and in lesson "9. ZeRO Stage 1 and 2", section
+ * "Know this" (stage 2 partitions optimizer state and gradients):
+ *
+ *   flatten   the tensor list into one vector of shard*world elements,
+ *             zero-padded at the end;
+ *   reduce    the world data-parallel gradient copies onto this rank's slice
+ *             (sum in rank order 0..world-1, then divide by world);
+ *   Adam      with bias correction on the fp32 master/m/v slice;
+ *   write     the updated slice into the flat parameter buffer (this rank's
+ *             all-gather contribution), as bf16 or fp32.
+ *
+ * Conventions for every function:
+ *   - The return value is a status: ZERO_OK (0) or a negative ZERO_E* code.
+ *     No function throws, aborts or exits. On failure, zero_last_error()
+ *     returns a message for the calling thread.
+ *   - Argument checks run before any device work; a call that fails a check
+ *     has launched nothing and changed nothing.
+ *   - "device pointer" means memory on the device the context was created
+ *     on (hipMalloc or a torch CUDA/HIP tensor's storage); "host array" means
+ *     ordinary host memory that is read during the call only.
+ *   - Device work is stream-ordered and asynchronous on the hipStream_t the
+ *     caller passes (0 = the null stream). A fault inside a kernel surfaces
+ *     at the caller's next synchronisation, not as a return code here.
+ *   - Element counts are int64: shards of more than 2^31 elements are fine.
+ *   - Misaligned device pointers are accepted (a slower path runs); only
+ *     bf16 (2-byte) and fp32 (4-byte) natural alignment is required.
+ *   - The library owns the context and its master/m/v buffers; the caller
+ *     owns every pointer it passes, and its streams.
+ */
+#ifndef ZERO_SHARD_H
+#define ZERO_SHARD_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct zero_ctx zero_ctx;   /* opaque, one per (rank, device) */
+
+typedef enum {
+    ZERO_F32 = 0,   /* IEEE binary32, 4 bytes */
+    ZERO_BF16 = 1   /* bfloat16 (top half of binary32), 2 bytes */
+} zero_dtype;
+
+enum {
+    ZERO_OK = 0,
+    ZERO_EINVAL = -1,        /* an argument is out of range or null */
+    ZERO_ENOMEM = -2,        /* device or host allocation failed */
+    ZERO_EHIP = -3,          /* a HIP runtime call failed */
+    ZERO_EUNSUPPORTED = -4   /* valid request this build cannot serve */
+};
+
+/* Largest world (number of gradient replicas) a step accepts. */
+#define ZERO_MAX_WORLD 256
+
+/* Shard geometry, host only ([ZeRO and FSDP], ZeroAdam constructor):
+ *   shard  = ceil(numel / world)     elements this rank owns
+ *   lo     = rank * shard            first flat index of its slice
+ *   padded = shard * world           length of the zero-padded flat vector
+ * Any out-pointer may be NULL. EINVAL unless numel >= 1, 1 <= world,
+ * 0 <= rank < world. */
+int zero_shard_geometry(int64_t numel, int32_t world, int32_t rank,
+                        int64_t *shard, int64_t *lo, int64_t *padded);
+
+/* Create a rank's context on the current HIP device: computes the
+ * geometry, allocates fp32 master, m and v of `shard` elements each and
+ * sets all three to zero (the page's m = v = 0; call zero_load_master to
+ * set master). Hyperparameters as in the page's constructor
+ * (lr, betas=(beta1, beta2), eps). Synchronous.
+ * EINVAL: geometry as above, !(0 < beta1 < 1), !(0 < beta2 < 1), eps < 0,
+ * lr or eps not finite, world > ZERO_MAX_WORLD, out == NULL.
+ * ENOMEM: device allocation failed. EHIP: no usable device. */
+int zero_shard_init(int64_t numel, int32_t world, int32_t rank,
+                    double lr, double beta1, double beta2, double eps,
+                    zero_ctx **out);
+
+/* Geometry of a context (any out-pointer may be NULL). */
+int zero_shard_info(const zero_ctx *ctx, int64_t *shard, int64_t *lo,
+                    int64_t *padded);
+
+/* Change the learning rate used by later steps (schedules). EINVAL if not
+ * finite. Host only. */
+int zero_set_lr(zero_ctx *ctx, double lr);
+
+/* master[i] = fp32(flat_params[flat_offset + i]) for i < shard, m = v = 0
+ * ([ZeRO and FSDP], ZeroAdam constructor: master is a copy of this rank's
+ * slice of the flattened parameters). flat_params: device pointer of
+ * `dtype` holding at least flat_offset + shard elements; flat_offset = lo
+ * for the full padded flat vector, 0 for a buffer holding the slice only.
+ * bf16 widens exactly. EINVAL: null pointer, unknown dtype, negative
+ * offset, or a buffer shorter than its allocation allows. */
+int zero_load_master(zero_ctx *ctx, const void *flat_params, zero_dtype dtype,
+                     int64_t flat_offset, hipStream_t stream);
+
+/* Flatten and pad ([ZeRO and FSDP], ZeroAdam._flatten): dst[k] is element
+ * k of the concatenation of srcs[0..ntensors) (each contiguous, row-major)
+ * for k < numel, and zero for numel <= k < padded. A bit copy: the dtype
+ * only fixes the element size. srcs: host array of ntensors device
+ * pointers (NULL allowed where numels[t] == 0); numels: host array;
+ * dst: device pointer to `padded` elements, which must not overlap any
+ * source. EINVAL unless ntensors >= 1, every numels[t] >= 0 and their sum
+ * equals the context's numel. */
+int zero_flatten(const zero_ctx *ctx, const void *const *srcs,
+                 const int64_t *numels, int32_t ntensors, zero_dtype dtype,
+                 void *dst, hipStream_t stream);
+
+/* The inverse ([ZeRO and FSDP], ZeroAdam.step, the copy of the gathered
+ * vector back into each parameter): dsts[t] receives flat elements
+ * [off_t, off_t + numels[t]) with off_t the sum of the earlier numels.
+ * Same argument rules as zero_flatten; the pad is not read. */
+int zero_unflatten(const zero_ctx *ctx, const void *flat, int32_t ntensors,
+                   const int64_t *numels, zero_dtype dtype,
+                   void *const *dsts, hipStream_t stream);
+
+/* One optimizer step on this rank's slice ([ZeRO and FSDP], ZeroAdam.step):
+ *   g      = (sum over q = 0..world-1, in that order, of
+ *             fp32(grad_replicas[q][grad_offset + i])) / world
+ *   m      = b1*m + (1-b1)*g ;  v = b2*v + (1-b2)*g*g
+ *   master = master - lr * (m/(1-b1^t)) / (sqrt(v/(1-b2^t)) + eps)
+ *   param_out[param_offset + i] = master, rounded to bf16 (nearest, ties to
+ *                                  even) or stored as fp32
+ * for every i < shard, all in binary32 with correctly rounded division and
+ * square root (the exact operation order is given in the library source).
+ * grad_replicas: host array of n_replicas device pointers (replica q =
+ * data-parallel rank q's gradient). grad_offset = lo when each replica is a
+ * full padded flat vector, 0 when it holds this rank's slice only; the same
+ * offset applies to every replica. param_out: device pointer; param_offset =
+ * lo for a full flat parameter buffer, 0 for a slice-only one.
+ * t >= 1 is the step number used for bias correction (the page's counter,
+ * incremented before use). Precondition: the pad elements of the replicas
+ * are zero (zero_flatten guarantees it); they are not masked.
+ * EINVAL: n_replicas != world, t < 1, NULL pointers, unknown dtypes. */
+int zero_step(zero_ctx *ctx, const void *const *grad_replicas,
+              int32_t n_replicas, zero_dtype grad_dtype, int64_t grad_offset,
+              void *param_out, zero_dtype param_dtype, int64_t param_offset,
+              int64_t t, hipStream_t stream);
+
+/* Copy the fp32 state out of / into the context (checkpoint and resume).
+ * master, m, v: device pointers to `shard` floats each; any may be NULL to
+ * skip that buffer. Stream-ordered device-to-device copies. */
+int zero_get_state(const zero_ctx *ctx, float *master, float *m, float *v,
+                   hipStream_t stream);
+int zero_set_state(zero_ctx *ctx, const float *master, const float *m,
+                   const float *v, hipStream_t stream);
+
+/* Model-state bytes per card for `numel` parameters and data-parallel
+ * degree `world` under mixed-precision Adam ([ZeRO and FSDP], table "The
+ * three stages"): stage 0 (plain data parallelism) 16*numel; 1: 4*numel +
+ * 12*numel/world; 2: 2*numel + 14*numel/world; 3: 16*numel/world.
+ * EINVAL for another stage, numel < 0, world < 1 or bytes == NULL. */
+int zero_state_bytes(int32_t stage, double numel, double world, double *bytes);
+
+/* Release the context and its device buffers (synchronises the device
+ * first). NULL is ignored. */
+void zero_destroy(zero_ctx *ctx);
+
+/* Message describing this thread's most recent failure ("" if none). The
+ * string stays valid until the next call on this thread. */
+const char *zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_SHARD_H */

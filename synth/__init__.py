@@ -109,13 +109,45 @@ def _gen(seed: int, device) -> torch.Generator:
     return g
 
 
+# Large draws are made in chunks of CHUNK elements so that the fp32 scratch
+# stays small; chunk c > 0 uses seed + c * 2^40 (chunk 0 uses the seed
+# itself, so draws of at most CHUNK elements are one plain draw).
+CHUNK = 1 << 27
+
+
+def _chunk_seed(seed: int, c: int) -> int:
+    return seed if c == 0 else seed + (c << 40)
+
+
+def fill_gaussian(out: torch.Tensor, std: float, seed: int,
+                  mseed: Optional[int] = None, frac: float = 0.01,
+                  scale: float = 100.0) -> torch.Tensor:
+    """Fill `out` (any float dtype, contiguous) with N(0, std) drawn in fp32
+    and cast with torch's round-to-nearest-even; with `mseed`, a
+    Bernoulli(frac) subset is multiplied by `scale` before the cast."""
+    flat = out.view(-1)
+    n = flat.numel()
+    dev = out.device
+    for c, start in enumerate(range(0, n, CHUNK)):
+        k = min(CHUNK, n - start)
+        x = torch.randn(k, generator=_gen(_chunk_seed(seed, c), dev),
+                        dtype=torch.float32, device=dev)
+        x.mul_(std)
+        if mseed is not None:
+            mask = torch.rand(k, generator=_gen(_chunk_seed(mseed, c), dev),
+                              device=dev) < frac
+            x[mask] *= scale
+            del mask
+        flat[start:start + k].copy_(x)
+        del x
+    return out
+
+
 def gaussian(n: int, std: float, seed: int, dtype=torch.float32,
              device="cpu") -> torch.Tensor:
     """n samples of N(0, std) drawn in fp32, then cast to `dtype`."""
-    x = torch.randn(n, generator=_gen(seed, device), dtype=torch.float32,
-                    device=device)
-    x.mul_(std)
-    return x if dtype == torch.float32 else x.to(dtype)
+    out = torch.empty(n, dtype=dtype, device=device)
+    return fill_gaussian(out, std, seed)
 
 
 def gaussian_with_outliers(n: int, std: float, seed: int, mseed: int,
@@ -123,12 +155,8 @@ def gaussian_with_outliers(n: int, std: float, seed: int, mseed: int,
                            dtype=torch.bfloat16, device="cpu") -> torch.Tensor:
     """N(0, std) in fp32; a Bernoulli(frac) subset is multiplied by `scale`
     before the cast to `dtype`."""
-    x = torch.randn(n, generator=_gen(seed, device), dtype=torch.float32,
-                    device=device)
-    x.mul_(std)
-    mask = torch.rand(n, generator=_gen(mseed, device), device=device) < frac
-    x[mask] *= scale
-    return x if dtype == torch.float32 else x.to(dtype)
+    out = torch.empty(n, dtype=dtype, device=device)
+    return fill_gaussian(out, std, seed, mseed, frac, scale)
 
 
 def params(n: int, device="cpu") -> torch.Tensor:
@@ -143,6 +171,17 @@ def split_to_shapes(flat: torch.Tensor, shapes) -> List[torch.Tensor]:
     for s in shapes:
         k = math.prod(s)
         out.append(flat[off:off + k].reshape(s).clone())
+        off += k
+    return out
+
+
+def split_views(flat: torch.Tensor, shapes) -> List[torch.Tensor]:
+    """Cut a 1-D tensor into contiguous views of `shapes` (no copies; for
+    lists too large to duplicate)."""
+    out, off = [], 0
+    for s in shapes:
+        k = math.prod(s)
+        out.append(flat[off:off + k].view(s))
         off += k
     return out
 

@@ -1,0 +1,378 @@
+// Host side of libzero.so: argument checks, the rank context (geometry,
+// hyperparameters, fp32 master/m/v), step scalars, and kernel dispatch.
+// The C ABI is declared and documented in include/zero.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/zero.h"
+#include "zero_internal.h"
+
+struct zero_ctx {
+    int64_t numel, shard, lo, padded;
+    int32_t world, rank;
+    double lr, beta1, beta2, eps;
+    int device;
+    int num_cus;
+    void *state;                 // one allocation: master | m | v
+    float *master, *m, *v;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+    return fail(ZERO_EHIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+bool valid_dtype(zero_dtype d) { return d == ZERO_F32 || d == ZERO_BF16; }
+size_t dtype_size(zero_dtype d) { return d == ZERO_BF16 ? 2 : 4; }
+
+int geometry(int64_t numel, int32_t world, int32_t rank, int64_t *shard, int64_t *lo,
+             int64_t *padded) {
+    if (numel < 1) return fail(ZERO_EINVAL, "numel must be >= 1 (got %lld)", (long long)numel);
+    if (world < 1) return fail(ZERO_EINVAL, "world must be >= 1 (got %d)", world);
+    if (rank < 0 || rank >= world)
+        return fail(ZERO_EINVAL, "rank must be in [0, world) (got rank %d, world %d)", rank, world);
+    const int64_t s = numel / world + (numel % world != 0 ? 1 : 0);
+    if (shard) *shard = s;
+    if (lo) *lo = (int64_t)rank * s;
+    if (padded) *padded = s * world;
+    return ZERO_OK;
+}
+
+// Make the context's device current for the duration of a call.
+class DeviceGuard {
+  public:
+    explicit DeviceGuard(int dev) {
+        if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+        if (prev_ != dev) err_ = hipSetDevice(dev);
+    }
+    ~DeviceGuard() {
+        if (prev_ >= 0 && err_ == hipSuccess) (void)hipSetDevice(prev_);
+    }
+    hipError_t error() const { return err_; }
+
+  private:
+    int prev_ = -1;
+    hipError_t err_ = hipSuccess;
+};
+
+// Reject a device range that runs past the allocation holding its first
+// byte (an undersized buffer would otherwise fault on the GPU). Memory the
+// runtime cannot describe (e.g. imported or virtually mapped) is accepted.
+int check_range(const void *p, int64_t nbytes, const char *what) {
+    if (nbytes <= 0) return ZERO_OK;
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    hipError_t e = hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return ZERO_OK;
+    }
+    const uintptr_t b = (uintptr_t)base, q = (uintptr_t)p;
+    if (q < b || q - b + (uint64_t)nbytes > (uint64_t)size)
+        return fail(ZERO_EINVAL, "%s: %lld bytes at %p run past the end of its allocation "
+                    "(%zu bytes at %p)", what, (long long)nbytes, p, size, (void *)base);
+    return ZERO_OK;
+}
+
+zk::StepScalars make_scalars(const zero_ctx *c, int64_t t) {
+    zk::StepScalars sc;
+    sc.b1 = (float)c->beta1;
+    sc.c1 = (float)(1.0 - c->beta1);
+    sc.b2 = (float)c->beta2;
+    sc.c2 = (float)(1.0 - c->beta2);
+    sc.lr = (float)c->lr;
+    sc.eps = (float)c->eps;
+    sc.bc1 = (float)(1.0 - std::pow(c->beta1, (double)t));
+    sc.bc2 = (float)(1.0 - std::pow(c->beta2, (double)t));
+    sc.nf = (float)c->world;
+    sc.n_pow2 = (c->world & (c->world - 1)) == 0;
+    sc.inv_n = (float)(1.0 / (double)c->world);
+    return sc;
+}
+
+int build_flat_segments(const zero_ctx *c, const void *const *tensors, const int64_t *numels,
+                        int32_t ntensors, zero_dtype dtype, const void *flat,
+                        std::vector<zk::Segment> &segs, bool to_flat) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (!tensors || !numels) return fail(ZERO_EINVAL, "null tensor or numel array");
+    if (ntensors < 1) return fail(ZERO_EINVAL, "ntensors must be >= 1 (got %d)", ntensors);
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dtype);
+    if (!flat) return fail(ZERO_EINVAL, "null flat buffer");
+    const int64_t es = (int64_t)dtype_size(dtype);
+    int64_t off = 0;
+    segs.clear();
+    segs.reserve((size_t)ntensors + 1);
+    for (int32_t t = 0; t < ntensors; ++t) {
+        const int64_t n = numels[t];
+        if (n < 0) return fail(ZERO_EINVAL, "numels[%d] is negative", t);
+        if (n > c->numel - off)
+            return fail(ZERO_EINVAL, "tensor sizes exceed the context's numel %lld",
+                        (long long)c->numel);
+        if (n > 0) {
+            if (!tensors[t]) return fail(ZERO_EINVAL, "tensor %d is null", t);
+            if ((uintptr_t)tensors[t] % (uintptr_t)es)
+                return fail(ZERO_EINVAL, "tensor %d is not %lld-byte aligned", t, (long long)es);
+            int rc = check_range(tensors[t], n * es, "tensor");
+            if (rc) return rc;
+            char *fp = (char *)flat + off * es;
+            if (to_flat) segs.push_back({tensors[t], fp, n * es});
+            else segs.push_back({fp, const_cast<void *>(tensors[t]), n * es});
+        }
+        off += n;
+    }
+    if (off != c->numel)
+        return fail(ZERO_EINVAL, "tensor sizes sum to %lld, context numel is %lld", (long long)off,
+                    (long long)c->numel);
+    if ((uintptr_t)flat % (uintptr_t)es)
+        return fail(ZERO_EINVAL, "flat buffer is not %lld-byte aligned", (long long)es);
+    int rc = check_range(flat, (to_flat ? c->padded : c->numel) * es, "flat buffer");
+    if (rc) return rc;
+    if (to_flat && c->padded > c->numel)
+        segs.push_back({nullptr, (char *)flat + c->numel * es, (c->padded - c->numel) * es});
+    return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *zero_last_error(void) { return g_last_error.c_str(); }
+
+int zero_shard_geometry(int64_t numel, int32_t world, int32_t rank, int64_t *shard, int64_t *lo,
+                        int64_t *padded) {
+    return geometry(numel, world, rank, shard, lo, padded);
+}
+
+int zero_state_bytes(int32_t stage, double numel, double world, double *bytes) {
+    if (!bytes) return fail(ZERO_EINVAL, "null output");
+    if (!(numel >= 0) || !(world >= 1)) return fail(ZERO_EINVAL, "need numel >= 0 and world >= 1");
+    switch (stage) {
+    case 0: *bytes = 16.0 * numel; break;                        // replicated
+    case 1: *bytes = 4.0 * numel + 12.0 * numel / world; break;  // optimizer state split
+    case 2: *bytes = 2.0 * numel + 14.0 * numel / world; break;  // + gradients split
+    case 3: *bytes = 16.0 * numel / world; break;                // + parameters split
+    default: return fail(ZERO_EINVAL, "stage must be 0..3 (got %d)", stage);
+    }
+    return ZERO_OK;
+}
+
+int zero_shard_init(int64_t numel, int32_t world, int32_t rank, double lr, double beta1,
+                    double beta2, double eps, zero_ctx **out) {
+    if (!out) return fail(ZERO_EINVAL, "null output pointer");
+    *out = nullptr;
+    int64_t shard, lo, padded;
+    int rc = geometry(numel, world, rank, &shard, &lo, &padded);
+    if (rc) return rc;
+    if (world > ZERO_MAX_WORLD)
+        return fail(ZERO_EINVAL, "world %d exceeds ZERO_MAX_WORLD (%d)", world, ZERO_MAX_WORLD);
+    if (!(beta1 > 0.0 && beta1 < 1.0) || !(beta2 > 0.0 && beta2 < 1.0))
+        return fail(ZERO_EINVAL, "betas must lie in (0, 1) (got %g, %g)", beta1, beta2);
+    if (!std::isfinite(lr)) return fail(ZERO_EINVAL, "lr must be finite");
+    if (!std::isfinite(eps) || eps < 0.0) return fail(ZERO_EINVAL, "eps must be finite and >= 0");
+
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+
+    zero_ctx *c = new (std::nothrow) zero_ctx();
+    if (!c) return fail(ZERO_ENOMEM, "host allocation failed");
+    c->numel = numel;
+    c->shard = shard;
+    c->lo = lo;
+    c->padded = padded;
+    c->world = world;
+    c->rank = rank;
+    c->lr = lr;
+    c->beta1 = beta1;
+    c->beta2 = beta2;
+    c->eps = eps;
+    c->device = dev;
+    c->num_cus = cus > 0 ? cus : 256;
+
+    // master | m | v, each segment rounded up to 256 bytes
+    const size_t seg = ((size_t)shard * sizeof(float) + 255) & ~(size_t)255;
+    e = hipMalloc(&c->state, 3 * seg);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        delete c;
+        return fail(ZERO_ENOMEM, "hipMalloc of %zu bytes for master/m/v failed: %s", 3 * seg,
+                    hipGetErrorString(e));
+    }
+    c->master = (float *)c->state;
+    c->m = (float *)((char *)c->state + seg);
+    c->v = (float *)((char *)c->state + 2 * seg);
+    e = hipMemset(c->state, 0, 3 * seg);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+    if (e != hipSuccess) {
+        (void)hipFree(c->state);
+        delete c;
+        return hip_fail(e, "clearing master/m/v");
+    }
+    *out = c;
+    return ZERO_OK;
+}
+
+int zero_shard_info(const zero_ctx *c, int64_t *shard, int64_t *lo, int64_t *padded) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (shard) *shard = c->shard;
+    if (lo) *lo = c->lo;
+    if (padded) *padded = c->padded;
+    return ZERO_OK;
+}
+
+int zero_set_lr(zero_ctx *c, double lr) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (!std::isfinite(lr)) return fail(ZERO_EINVAL, "lr must be finite");
+    c->lr = lr;
+    return ZERO_OK;
+}
+
+int zero_load_master(zero_ctx *c, const void *flat, zero_dtype dtype, int64_t flat_offset,
+                     hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (!flat) return fail(ZERO_EINVAL, "null flat parameter buffer");
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dtype);
+    if (flat_offset < 0) return fail(ZERO_EINVAL, "negative offset");
+    const size_t es = dtype_size(dtype);
+    if ((uintptr_t)flat % es) return fail(ZERO_EINVAL, "flat buffer misaligned for its dtype");
+    int rc = check_range(flat, (flat_offset + c->shard) * (int64_t)es, "flat parameter buffer");
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    const char *base = (const char *)flat + (size_t)flat_offset * es;
+    hipError_t e = zk::launch_load_master(base, dtype == ZERO_BF16, c->master, c->m, c->v,
+                                          c->shard, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "load_master launch");
+}
+
+int zero_flatten(const zero_ctx *c, const void *const *srcs, const int64_t *numels,
+                 int32_t ntensors, zero_dtype dtype, void *dst, hipStream_t stream) {
+    std::vector<zk::Segment> segs;
+    int rc = build_flat_segments(c, srcs, numels, ntensors, dtype, dst, segs, true);
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    hipError_t e = zk::launch_copy_segments(segs.data(), (int)segs.size(),
+                                            (int)dtype_size(dtype), stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "flatten launch");
+}
+
+int zero_unflatten(const zero_ctx *c, const void *flat, int32_t ntensors, const int64_t *numels,
+                   zero_dtype dtype, void *const *dsts, hipStream_t stream) {
+    std::vector<zk::Segment> segs;
+    int rc = build_flat_segments(c, (const void *const *)dsts, numels, ntensors, dtype, flat,
+                                 segs, false);
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    hipError_t e = zk::launch_copy_segments(segs.data(), (int)segs.size(),
+                                            (int)dtype_size(dtype), stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "unflatten launch");
+}
+
+int zero_step(zero_ctx *c, const void *const *grads, int32_t n_replicas, zero_dtype grad_dtype,
+              int64_t grad_offset, void *param_out, zero_dtype param_dtype, int64_t param_offset,
+              int64_t t, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (n_replicas != c->world)
+        return fail(ZERO_EINVAL, "n_replicas (%d) must equal world (%d)", n_replicas, c->world);
+    if (t < 1) return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
+    if (!grads) return fail(ZERO_EINVAL, "null replica array");
+    if (!param_out) return fail(ZERO_EINVAL, "null parameter output");
+    if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
+        return fail(ZERO_EINVAL, "unknown dtype");
+    if (grad_offset < 0 || param_offset < 0) return fail(ZERO_EINVAL, "negative offset");
+    const size_t ge = dtype_size(grad_dtype), pe = dtype_size(param_dtype);
+    const void *slices[ZERO_MAX_WORLD];
+    for (int q = 0; q < n_replicas; ++q) {
+        if (!grads[q]) return fail(ZERO_EINVAL, "replica %d is null", q);
+        if ((uintptr_t)grads[q] % ge) return fail(ZERO_EINVAL, "replica %d misaligned", q);
+        slices[q] = (const char *)grads[q] + (size_t)grad_offset * ge;
+        int rc = check_range(grads[q], (grad_offset + c->shard) * (int64_t)ge, "gradient replica");
+        if (rc) return rc;
+    }
+    if ((uintptr_t)param_out % pe) return fail(ZERO_EINVAL, "parameter output misaligned");
+    int rc = check_range(param_out, (param_offset + c->shard) * (int64_t)pe, "parameter output");
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+
+    zk::StepArgs a;
+    a.grads = slices;
+    a.n = n_replicas;
+    a.grad_bf16 = grad_dtype == ZERO_BF16;
+    a.master = c->master;
+    a.m = c->m;
+    a.v = c->v;
+    a.out = (char *)param_out + (size_t)param_offset * pe;
+    a.out_bf16 = param_dtype == ZERO_BF16;
+    a.shard = c->shard;
+    a.sc = make_scalars(c, t);
+    a.num_cus = c->num_cus;
+    hipError_t e = zk::launch_step(a, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "step launch");
+}
+
+static int copy_state(const zero_ctx *c, const float *const src[3], float *const dst[3],
+                      hipStream_t stream, const char *what) {
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    for (int k = 0; k < 3; ++k) {
+        if (!src[k] || !dst[k]) continue;
+        int rc = check_range(src[k], c->shard * (int64_t)sizeof(float), what);
+        if (!rc) rc = check_range(dst[k], c->shard * (int64_t)sizeof(float), what);
+        if (rc) return rc;
+        hipError_t e = hipMemcpyAsync(dst[k], src[k], (size_t)c->shard * sizeof(float),
+                                      hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, what);
+    }
+    return ZERO_OK;
+}
+
+int zero_get_state(const zero_ctx *c, float *master, float *m, float *v, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    const float *src[3] = {c->master, c->m, c->v};
+    float *dst[3] = {master, m, v};
+    return copy_state(c, src, dst, stream, "get_state copy");
+}
+
+int zero_set_state(zero_ctx *c, const float *master, const float *m, const float *v,
+                   hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    const float *src[3] = {master, m, v};
+    float *dst[3] = {c->master, c->m, c->v};
+    return copy_state(c, src, dst, stream, "set_state copy");
+}
+
+void zero_destroy(zero_ctx *c) {
+    if (!c) return;
+    DeviceGuard g(c->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(c->state);
+    delete c;
+}
+
+}  // extern "C"

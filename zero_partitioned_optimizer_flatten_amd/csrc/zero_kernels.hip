@@ -1,0 +1,430 @@
+// gfx950 kernels for one rank's ZeRO-2 optimizer step.
+//
+// K2  fused step: reduce the N gradient replicas onto this rank's slice,
+//     Adam with bias correction on fp32 master/m/v, write the slice back as
+//     bf16 or fp32 -- one pass over HBM, every intermediate in registers.
+// K1  batched segment copy: flatten (tensor list -> zero-padded flat vector)
+//     and its inverse are lists of (src, dst, bytes) segments.
+// K0  master initialisation from the flat parameters.
+//
+// The update follows the page "ZeRO and FSDP: partitioning the optimizer
+// states, the gradients and the parameters" (AI infra handbook), section
+// "Implementing ZeRO's Adam from scratch", ZeroAdam.step, in binary32 with
+// the operation order PyTorch uses for those lines on a CPU:
+//     g  = (g_0 + g_1 + ... + g_{N-1}) / N          (left fold, rank order)
+//     m  = fma(g, 1-b1, m*b1)
+//     v  = fma((1-b2)*g, g, v*b2)
+//     mh = m / (1-b1^t);  vh = v / (1-b2^t)
+//     master = master - (lr*mh) / (sqrt(vh) + eps)
+// Division and square root are the correctly rounded IEEE operations (this
+// file is built with -fhip-fp32-correctly-rounded-divide-sqrt and
+// -ffp-contract=off; f32 denormals are kept). The step is HBM-bound
+// (about 0.5 flop per byte), so the kernels are written for streaming:
+// 16-byte loads and stores, coalesced across each 64-lane wavefront, with
+// every replica's load for a vector issued before the fold consumes it.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zero_internal.h"
+
+namespace zk {
+
+namespace {
+
+constexpr int kBlock = 256;          // 4 wavefronts of 64 lanes
+constexpr int kVec = 8;              // elements per lane per vector step
+constexpr int kGroup = 8;            // replicas loaded together
+
+__device__ __forceinline__ float widen_bf16(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// binary32 -> bf16 bits, round to nearest, ties to even. NaN keeps its sign
+// and gets the quiet bit; overflow rounds to infinity through the carry.
+__device__ __forceinline__ uint32_t round_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    uint32_t r = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
+}
+
+// One element of the Adam update; p/m/v updated in place.
+__device__ __forceinline__ void adam_update(float g, float &p, float &m,
+                                            float &v, const StepScalars &sc) {
+    float mm = __builtin_fmaf(g, sc.c1, m * sc.b1);
+    float vv = __builtin_fmaf(sc.c2 * g, g, v * sc.b2);
+    float mh = mm / sc.bc1;
+    float vh = vv / sc.bc2;
+    float den = __builtin_sqrtf(vh) + sc.eps;
+    float u = (sc.lr * mh) / den;
+    m = mm;
+    v = vv;
+    p = p - u;
+}
+
+// Replica pointer table passed by value in the kernel arguments, so each
+// pointer is a wave-uniform scalar (SGPR base + per-lane offset).
+template <int NR>
+struct Reps {
+    const void *p[NR > 0 ? NR : ZERO_MAX_WORLD];
+};
+
+// Raw 8-element gradient vector of one replica: 16 bytes of bf16 or 32
+// bytes of fp32.
+template <bool GB> struct RawVec;
+template <> struct RawVec<true> { uint4 a; };
+template <> struct RawVec<false> { float4 a, b; };
+
+template <bool GB>
+__device__ __forceinline__ RawVec<GB> load_vec(const void *base, int64_t j);
+
+template <>
+__device__ __forceinline__ RawVec<true> load_vec<true>(const void *base, int64_t j) {
+    RawVec<true> r;
+    r.a = reinterpret_cast<const uint4 *>(base)[j];
+    return r;
+}
+
+template <>
+__device__ __forceinline__ RawVec<false> load_vec<false>(const void *base, int64_t j) {
+    RawVec<false> r;
+    const float4 *p = reinterpret_cast<const float4 *>(base);
+    r.a = p[2 * j];
+    r.b = p[2 * j + 1];
+    return r;
+}
+
+__device__ __forceinline__ void unpack(const RawVec<true> &r, float (&x)[kVec]) {
+    x[0] = widen_bf16(r.a.x & 0xFFFFu); x[1] = widen_bf16(r.a.x >> 16);
+    x[2] = widen_bf16(r.a.y & 0xFFFFu); x[3] = widen_bf16(r.a.y >> 16);
+    x[4] = widen_bf16(r.a.z & 0xFFFFu); x[5] = widen_bf16(r.a.z >> 16);
+    x[6] = widen_bf16(r.a.w & 0xFFFFu); x[7] = widen_bf16(r.a.w >> 16);
+}
+
+__device__ __forceinline__ void unpack(const RawVec<false> &r, float (&x)[kVec]) {
+    x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+    x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
+}
+
+__device__ __forceinline__ void load8(const float *base, int64_t j, float (&x)[kVec]) {
+    const float4 *p = reinterpret_cast<const float4 *>(base);
+    float4 a = p[2 * j], b = p[2 * j + 1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store8(float *base, int64_t j, const float (&x)[kVec]) {
+    float4 *p = reinterpret_cast<float4 *>(base);
+    p[2 * j] = make_float4(x[0], x[1], x[2], x[3]);
+    p[2 * j + 1] = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// Fold one group of up to kGroup replicas into s (rank order). The group's
+// loads are all issued before the first add consumes them.
+template <int NR, bool GB>
+__device__ __forceinline__ void fold_group(const Reps<NR> &reps, int q0, int n, int64_t j,
+                                           float (&s)[kVec]) {
+    RawVec<GB> raw[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k)
+        if (q0 + k < n) raw[k] = load_vec<GB>(reps.p[q0 + k], j);
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        if (q0 + k < n) {
+            float x[kVec];
+            unpack(raw[k], x);
+            if (q0 + k == 0) {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) s[e] = x[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) s[e] = s[e] + x[e];
+            }
+        }
+    }
+}
+
+// Vector path: every stream 16-byte aligned; lane handles elements
+// [8j, 8j+8) of vector j, vectors strided over the whole grid.
+// NR > 0 fixes the replica count at compile time (N <= 16 fully unrolled;
+// larger N walks the groups in a loop to bound register use); NR == 0 reads
+// it from `nrep`.
+template <int NR, bool GB, bool PB>
+__global__ void __launch_bounds__(kBlock)
+step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
+                float *__restrict__ mom, float *__restrict__ var,
+                void *__restrict__ out, int64_t nvec, StepScalars sc) {
+    const int n = NR > 0 ? NR : nrep;
+    constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
+    const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < nvec; j += stride) {
+        float p[kVec], m[kVec], v[kVec];
+        load8(master, j, p);
+        load8(mom, j, m);
+        load8(var, j, v);
+
+        float s[kVec];
+        if constexpr (NR > 0 && NR <= 2 * kGroup) {
+#pragma unroll
+            for (int q0 = 0; q0 < NR; q0 += kGroup) fold_group<NR, GB>(reps, q0, NR, j, s);
+        } else {
+#pragma unroll 1
+            for (int q0 = 0; q0 < n; q0 += kGroup) fold_group<NR, GB>(reps, q0, n, j, s);
+        }
+
+        float g[kVec];
+        if (pow2) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;   // exact scaling
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
+
+        store8(master, j, p);
+        store8(mom, j, m);
+        store8(var, j, v);
+        if (PB) {
+            uint4 o;
+            o.x = round_bf16(p[0]) | (round_bf16(p[1]) << 16);
+            o.y = round_bf16(p[2]) | (round_bf16(p[3]) << 16);
+            o.z = round_bf16(p[4]) | (round_bf16(p[5]) << 16);
+            o.w = round_bf16(p[6]) | (round_bf16(p[7]) << 16);
+            reinterpret_cast<uint4 *>(out)[j] = o;
+        } else {
+            store8(reinterpret_cast<float *>(out), j, p);
+        }
+    }
+}
+
+// Element path: any alignment, and the tail of the vector path. Lane
+// handles element i, consecutive lanes consecutive elements.
+template <bool GB, bool PB>
+__global__ void __launch_bounds__(kBlock)
+step_elem_kernel(Reps<0> reps, int nrep, float *__restrict__ master,
+                 float *__restrict__ mom, float *__restrict__ var,
+                 void *__restrict__ out, int64_t begin, int64_t end,
+                 StepScalars sc) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = begin + (int64_t)blockIdx.x * kBlock + threadIdx.x; i < end; i += stride) {
+        float s;
+        if (GB) s = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[0])[i]);
+        else s = reinterpret_cast<const float *>(reps.p[0])[i];
+        for (int q = 1; q < nrep; ++q) {
+            float x;
+            if (GB) x = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[q])[i]);
+            else x = reinterpret_cast<const float *>(reps.p[q])[i];
+            s = s + x;
+        }
+        float p = master[i], m = mom[i], v = var[i];
+        const float g = sc.n_pow2 ? s * sc.inv_n : s / sc.nf;
+        adam_update(g, p, m, v, sc);
+        master[i] = p;
+        mom[i] = m;
+        var[i] = v;
+        if (PB) reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)round_bf16(p);
+        else reinterpret_cast<float *>(out)[i] = p;
+    }
+}
+
+template <int NR, bool GB, bool PB>
+hipError_t launch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
+    Reps<NR> reps;
+    for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
+    int64_t want = (nvec + kBlock - 1) / kBlock;
+    int64_t cap = (int64_t)a.num_cus * 8;
+    int grid = (int)(want < cap ? want : cap);
+    hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB>), dim3(grid), dim3(kBlock), 0,
+                       stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, a.sc);
+    return hipGetLastError();
+}
+
+template <bool GB, bool PB>
+hipError_t dispatch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
+    switch (a.n) {
+    case 1: return launch_vec<1, GB, PB>(a, nvec, stream);
+    case 2: return launch_vec<2, GB, PB>(a, nvec, stream);
+    case 4: return launch_vec<4, GB, PB>(a, nvec, stream);
+    case 8: return launch_vec<8, GB, PB>(a, nvec, stream);
+    case 16: return launch_vec<16, GB, PB>(a, nvec, stream);
+    case 64: return launch_vec<64, GB, PB>(a, nvec, stream);
+    default: return launch_vec<0, GB, PB>(a, nvec, stream);
+    }
+}
+
+template <bool GB, bool PB>
+hipError_t launch_elem(const StepArgs &a, int64_t begin, int64_t end, hipStream_t stream) {
+    Reps<0> reps;
+    for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
+    int64_t want = (end - begin + kBlock - 1) / kBlock;
+    int64_t cap = (int64_t)a.num_cus * 8;
+    int grid = (int)(want < cap ? want : cap);
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL((step_elem_kernel<GB, PB>), dim3(grid), dim3(kBlock), 0, stream,
+                       reps, a.n, a.master, a.m, a.v, a.out, begin, end, a.sc);
+    return hipGetLastError();
+}
+
+template <bool GB, bool PB>
+hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
+    bool aligned = ((uintptr_t)a.out % 16) == 0 && ((uintptr_t)a.master % 16) == 0 &&
+                   ((uintptr_t)a.m % 16) == 0 && ((uintptr_t)a.v % 16) == 0;
+    for (int q = 0; q < a.n && aligned; ++q) aligned = ((uintptr_t)a.grads[q] % 16) == 0;
+    int64_t nvec = aligned ? a.shard / kVec : 0;
+    if (nvec > 0) {
+        hipError_t e = dispatch_vec<GB, PB>(a, nvec, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (nvec * kVec < a.shard) return launch_elem<GB, PB>(a, nvec * kVec, a.shard, stream);
+    return hipSuccess;
+}
+
+// ------------------------------------------------------------ segment copy
+
+constexpr int kSegBatch = 64;                 // segments per launch
+constexpr int64_t kChunk = 65536;             // bytes per workgroup
+
+struct SegBatch {
+    const char *src[kSegBatch];
+    char *dst[kSegBatch];
+    int64_t nbytes[kSegBatch];
+    int64_t blk0[kSegBatch + 1];              // prefix of workgroup counts
+    int nseg;
+    int esize;
+};
+
+template <typename T>
+__device__ __forceinline__ void copy_elems(const char *src, char *dst, int64_t nbytes) {
+    const int64_t n = nbytes / (int64_t)sizeof(T);
+    for (int64_t k = threadIdx.x; k < n; k += kBlock) {
+        T x = src ? reinterpret_cast<const T *>(src)[k] : T(0);
+        reinterpret_cast<T *>(dst)[k] = x;
+    }
+}
+
+__device__ __forceinline__ void copy_elems_any(const char *src, char *dst, int64_t nbytes, int esize) {
+    if (esize == 4) copy_elems<uint32_t>(src, dst, nbytes);
+    else copy_elems<uint16_t>(src, dst, nbytes);
+}
+
+// Workgroup w copies one kChunk-byte chunk of one segment. Source and
+// destination with the same offset within 16 bytes take 16-byte vectors
+// after a short element-wise head; otherwise the chunk is copied element by
+// element (consecutive lanes, consecutive elements).
+__global__ void __launch_bounds__(kBlock) copy_segments_kernel(SegBatch b) {
+    const int64_t w = blockIdx.x;
+    int lo = 0, hi = b.nseg - 1;              // last segment with blk0 <= w
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (b.blk0[mid] <= w) lo = mid;
+        else hi = mid - 1;
+    }
+    const int s = lo;
+    const int64_t beg = (w - b.blk0[s]) * kChunk;
+    int64_t len = b.nbytes[s] - beg;
+    if (len > kChunk) len = kChunk;
+    if (len <= 0) return;
+    const char *src = b.src[s] ? b.src[s] + beg : nullptr;
+    char *dst = b.dst[s] + beg;
+
+    const unsigned da = (unsigned)((uintptr_t)dst & 15u);
+    const unsigned sa = src ? (unsigned)((uintptr_t)src & 15u) : da;
+    if (sa != da) {
+        copy_elems_any(src, dst, len, b.esize);
+        return;
+    }
+    int64_t head = (int64_t)((16u - da) & 15u);
+    if (head > len) head = len;
+    copy_elems_any(src, dst, head, b.esize);
+    const int64_t nv = (len - head) / 16;
+    const uint4 *s4 = src ? reinterpret_cast<const uint4 *>(src + head) : nullptr;
+    uint4 *d4 = reinterpret_cast<uint4 *>(dst + head);
+    int64_t k = threadIdx.x;
+    if (s4) {
+        for (; k + 3 * kBlock < nv; k += 4 * kBlock) {
+            uint4 x0 = s4[k], x1 = s4[k + kBlock], x2 = s4[k + 2 * kBlock], x3 = s4[k + 3 * kBlock];
+            d4[k] = x0;
+            d4[k + kBlock] = x1;
+            d4[k + 2 * kBlock] = x2;
+            d4[k + 3 * kBlock] = x3;
+        }
+        for (; k < nv; k += kBlock) d4[k] = s4[k];
+    } else {
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        for (; k < nv; k += kBlock) d4[k] = z;
+    }
+    const int64_t done = head + nv * 16;
+    copy_elems_any(src ? src + done : nullptr, dst + done, len - done, b.esize);
+}
+
+// ---------------------------------------------------------- master load
+
+template <bool FB>
+__global__ void __launch_bounds__(kBlock)
+load_master_kernel(const void *__restrict__ flat, float *__restrict__ master,
+                   float *__restrict__ mom, float *__restrict__ var, int64_t shard) {
+    const int64_t stride = (int64_t)gridDim.x * kBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < shard; i += stride) {
+        master[i] = FB ? widen_bf16(reinterpret_cast<const uint16_t *>(flat)[i])
+                       : reinterpret_cast<const float *>(flat)[i];
+        mom[i] = 0.0f;
+        var[i] = 0.0f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepArgs &a, hipStream_t stream) {
+    if (a.shard <= 0) return hipSuccess;
+    if (a.grad_bf16) {
+        return a.out_bf16 ? step_typed<true, true>(a, stream) : step_typed<true, false>(a, stream);
+    }
+    return a.out_bf16 ? step_typed<false, true>(a, stream) : step_typed<false, false>(a, stream);
+}
+
+hipError_t launch_copy_segments(const Segment *segs, int nseg, int esize, hipStream_t stream) {
+    int i = 0;
+    while (i < nseg) {
+        SegBatch b;
+        b.esize = esize;
+        b.nseg = 0;
+        int64_t blocks = 0;
+        while (i < nseg && b.nseg < kSegBatch) {
+            const Segment &s = segs[i++];
+            if (s.nbytes <= 0) continue;
+            b.src[b.nseg] = static_cast<const char *>(s.src);
+            b.dst[b.nseg] = static_cast<char *>(s.dst);
+            b.nbytes[b.nseg] = s.nbytes;
+            b.blk0[b.nseg] = blocks;
+            blocks += (s.nbytes + kChunk - 1) / kChunk;
+            b.nseg++;
+        }
+        if (b.nseg == 0) continue;
+        b.blk0[b.nseg] = blocks;
+        // a dispatch holds at most 2^32-1 work-items: 2^24 workgroups of 64 KiB
+        if (blocks > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(copy_segments_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+                           stream, b);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_load_master(const void *flat, bool flat_bf16, float *master, float *m,
+                              float *v, int64_t shard, hipStream_t stream) {
+    if (shard <= 0) return hipSuccess;
+    int64_t want = (shard + kBlock - 1) / kBlock;
+    int grid = (int)(want < 65536 ? want : 65536);
+    if (flat_bf16)
+        hipLaunchKernelGGL(load_master_kernel<true>, dim3(grid), dim3(kBlock), 0, stream, flat,
+                           master, m, v, shard);
+    else
+        hipLaunchKernelGGL(load_master_kernel<false>, dim3(grid), dim3(kBlock), 0, stream, flat,
+                           master, m, v, shard);
+    return hipGetLastError();
+}
+
+}  // namespace zk
