@@ -1,0 +1,248 @@
+"""Benchmark: one data-parallel rank's ZeRO-2 step on the 7e9-parameter,
+N = 8, rank-0 shard (875,000,000 elements), on one MI355X.
+
+A timed step is one pass of the whole hot path over one batch of gradients:
+  1. flatten this rank's gradient (the 7e9-element flat vector, a one-tensor
+     list) into its zero-padded flat buffer            -> flatten kernel
+  2. reduce the 8 replicas onto the slice, Adam with bias correction on the
+     fp32 master/m/v, write the bf16 slice into the full flat parameter
+     buffer                                            -> fused step kernel
+Replica 0 is the buffer step 1 wrote; replicas 1..7 (the other ranks'
+contributions to this slice) are slice-only buffers. All inputs are seeded
+synthetic data resident in HBM before timing starts.
+
+Prints one JSON line. `value` is shard elements updated per second over the
+whole step; `roofline` describes the fused step kernel (HIP events on the
+launch stream); `cpu_baseline` times the CPU oracle on a bounded window of
+the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+import zero_partitioned_optimizer_flatten_amd as zero  # noqa: E402
+
+NUMEL, WORLD, RANK = 7_000_000_000, 8, 0
+LR, BETAS, EPS = 1e-3, (0.9, 0.999), 1e-8
+PEAK_HBM_GBPS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "zero_partitioned_optimizer_flatten_amd", "csrc",
+                          "zero_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_step_flat7b_n8.md")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def step_bytes_per_elem(world, grad_bytes=2, param_bytes=2):
+    """Algorithmic bytes per shard element of the fused step: read the N
+    replica values, read and write fp32 master/m/v, write the parameter."""
+    return world * grad_bytes + 12 + 12 + param_bytes
+
+
+def kernel_source_digest():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per fused-step launch from the committed rocprofv3 counter
+    summary, or None if absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    src = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not src or not val or src.group(1) != kernel_source_digest():
+        return None
+    return float(val.group(1))
+
+
+def cpu_baseline(window: int, min_seconds: float):
+    """The CPU oracle as it stands, on a window of the same workload: the
+    flatten of the matching 8*window gradient elements plus the shard step
+    on `window` elements with all 8 replicas, repeated for min_seconds."""
+    import oracle
+    rng_g = torch.Generator().manual_seed(1)
+    own = (torch.randn(WORLD * window, generator=rng_g) * 1e-3).to(torch.bfloat16)
+    own_bits = own.view(torch.int16).numpy().view(np.uint16)
+    peers = [(torch.randn(window, generator=rng_g) * 1e-3).to(torch.bfloat16)
+             .view(torch.int16).numpy().view(np.uint16).copy() for _ in range(WORLD - 1)]
+    orc = oracle.ShardOracle(window, 1, 0, LR, BETAS, EPS, n_replicas=WORLD)
+    orc.master[:] = (torch.randn(window, generator=rng_g) * 0.02).numpy()
+    out = np.zeros(window, np.uint16)
+    iters, t = 0, 1
+    t0 = time.perf_counter()
+    while True:
+        flat = oracle.flatten([own_bits], WORLD * window)
+        orc.step([flat[:window]] + peers, t, out, grad_offset=0, out_offset=0)
+        iters += 1
+        t += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds and iters >= 2:
+            break
+    return dict(value=window * iters / el, unit="shard elements/s", cores=oracle.num_threads(),
+                kind="oracle",
+                sample=(f"{iters} steps of a {window}-element window of the 7e9/N=8 shard: "
+                        f"flatten of {WORLD * window} bf16 gradient elements + reduce/Adam/bf16 "
+                        f"over {WORLD} replicas, {el:.1f} s wall"))
+
+
+def copy_ceiling(nbytes: int, reps: int = 5):
+    """torch device-to-device copy as a plain-copy context figure."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-window", type=int, default=1 << 24)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the plain-copy context measurement")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one rank's shard step on one GPU; runs on more than one "
+              "GPU are not supported by this build (the other ranks are simulated as "
+              "gradient replicas on the same device).", file=sys.stderr)
+        sys.exit(2)
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    zero.lib()
+
+    st = zero.ShardState(NUMEL, WORLD, RANK, LR, BETAS, EPS)
+    S, lo, P = st.shard, st.lo, st.padded
+    log(f"shard={S} lo={lo} padded={P}; generating inputs")
+    p = synth.gaussian(S, synth.PARAM_STD, synth.PARAM_SEED, torch.float32, dev)
+    st.load_master(p, flat_offset=0)
+    del p
+    own_grad = torch.empty(NUMEL, dtype=torch.bfloat16, device=dev)
+    synth.fill_gaussian(own_grad, 1e-3, synth.grad_seed(1, RANK))
+    own_flat = torch.empty(P, dtype=torch.bfloat16, device=dev)
+    peers = []
+    for q in range(WORLD):
+        if q == RANK:
+            continue
+        r = torch.empty(S, dtype=torch.bfloat16, device=dev)
+        synth.fill_gaussian(r, 1e-3, synth.grad_seed(1, q))
+        peers.append(r)
+    reps = peers[:RANK] + [own_flat[lo:lo + S]] + peers[RANK:]
+    params_full = torch.zeros(P, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    log("inputs resident; warming up")
+
+    stream = torch.cuda.current_stream()
+    n_total = args.warmup + args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_total)]
+    for i in range(args.warmup):
+        ev[i][0].record(stream)
+        st.flatten([own_grad], own_flat)
+        ev[i][1].record(stream)
+        st.step(reps, i + 1, params_full, grad_offset=0, param_offset=lo)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.warmup, n_total):
+        ev[i][0].record(stream)
+        st.flatten([own_grad], own_flat)
+        ev[i][1].record(stream)
+        st.step(reps, i + 1, params_full, grad_offset=0, param_offset=lo)
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    flat_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n_total)])
+    step_ms = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.warmup, n_total)])
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = S * args.steps / wall
+    bpe = step_bytes_per_elem(WORLD)
+    k2_bytes = bpe * S
+    k1_bytes = 2 * NUMEL + 2 * P
+    k2_gbps = k2_bytes / (step_ms.mean() * 1e-3) / 1e9
+    k1_gbps = k1_bytes / (flat_ms.mean() * 1e-3) / 1e9
+    traffic = measured_traffic()
+
+    # the step must have produced finite, changing parameters
+    assert torch.isfinite(params_full[:S].float()).all().item()
+
+    del own_grad, own_flat, peers, reps, params_full
+    st.close()
+    torch.cuda.empty_cache()
+
+    context = {}
+    if not args.no_context:
+        context["torch_copy_gbps"] = round(copy_ceiling(8 << 30), 1)
+
+    result = {
+        "metric": "sharded Adam step: elements/s and achieved HBM GB/s (% of peak), 7B N=8",
+        "value": value,
+        "unit": "shard elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 (bf16 gradients and parameter output)",
+        "data": "synthetic: seeded N(0,1e-3) bf16 gradients, N(0,0.02) fp32 parameters",
+        "config": {"workload": "flat7b_n8_rank0: 7e9-element flat vector, N=8 simulated "
+                               "ranks, rank 0 shard of 875,000,000",
+                   "numel": NUMEL, "world": WORLD, "rank": RANK, "shard": S,
+                   "global_batch": None, "seq_len": None, "parallelism": "zero2-shard, 1 GPU"},
+        "step_hbm_gbps": (k1_bytes + k2_bytes) / (ms_per_step * 1e-3) / 1e9,
+        "kernels": {
+            "fused_step": {"ms_mean": float(step_ms.mean()), "ms_min": float(step_ms.min()),
+                           "bytes_per_launch": k2_bytes, "bytes_per_elem": bpe,
+                           "gbps": k2_gbps, "elements_per_s": S / (step_ms.mean() * 1e-3)},
+            "flatten": {"ms_mean": float(flat_ms.mean()), "ms_min": float(flat_ms.min()),
+                        "bytes_per_launch": k1_bytes, "gbps": k1_gbps},
+        },
+        "roofline": {"bound": "hbm", "achieved": k2_gbps, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": k2_gbps / PEAK_HBM_GBPS,
+                     "traffic": traffic,
+                     "kernel": "fused reduce+Adam+bf16 step (step_vec_kernel<8,bf16,bf16>)"},
+        "context": context,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_window, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -136,3 +136,21 @@ def test_llama13b_n8_last_rank_full_size():
     tail = bits(st.get_state()[0][valid:])
     assert not np.any(tail.view(np.uint32)), "pad master not zero"
     st.close()
+
+
+def test_flatten_single_tensor_beyond_one_dispatch():
+    """A one-tensor list of 9,000,000,001 bf16 elements (18 GB) flattened
+    to 9,000,000,008 (N = 8): longer than one copy dispatch may cover, so
+    the library splits it; result bit-exact and pad zero."""
+    dev = torch.device("cuda")
+    numel, world = 9_000_000_001, 8
+    st = zero.ShardState(numel, world, 0, LR)
+    src = torch.empty(numel, dtype=torch.bfloat16, device=dev)
+    synth.fill_gaussian(src, 1.0, 3)
+    dst = torch.full((st.padded,), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    st.flatten([src], dst)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:numel].view(torch.int16), src.view(torch.int16))
+    assert not torch.any(dst[numel:].view(torch.int16))
+    log("flatten of an 18 GB tensor bit-exact")
+    st.close()

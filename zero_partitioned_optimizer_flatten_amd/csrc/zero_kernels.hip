@@ -31,9 +31,102 @@ namespace zk {
 
 namespace {
 
-constexpr int kBlock = 256;          // 4 wavefronts of 64 lanes
+#ifndef ZK_BLOCK
+#define ZK_BLOCK 512
+#endif
+constexpr int kBlock = ZK_BLOCK;     // workgroup size (wavefronts of 64 lanes)
 constexpr int kVec = 8;              // elements per lane per vector step
 constexpr int kGroup = 8;            // replicas loaded together
+
+// Launch shape of the fused step: each workgroup owns kStepVpt * kBlock
+// consecutive 8-element vectors (one pass, no grid-stride loop), so the
+// waves in flight at any moment cover one contiguous, sliding window of
+// every stream. ZK_STEP_VPT=0 selects a persistent grid-stride launch;
+// ZK_STEP_VPT=-1 a persistent launch of ZK_STEP_BPC workgroups per CU in
+// which each workgroup walks its own contiguous range.
+#ifndef ZK_STEP_VPT
+#define ZK_STEP_VPT 1
+#endif
+#ifndef ZK_STEP_BPC
+#define ZK_STEP_BPC 8
+#endif
+// Non-temporal (streaming) hints: every stream is touched once per step.
+#ifndef ZK_NT_GRAD
+#define ZK_NT_GRAD 1
+#endif
+#ifndef ZK_NT_STATE
+#define ZK_NT_STATE 0
+#endif
+#ifndef ZK_NT_OUT
+#define ZK_NT_OUT 1
+#endif
+// Non-temporal stores (only) for master/m/v.
+#ifndef ZK_NT_STATE_ST
+#define ZK_NT_STATE_ST 0
+#endif
+// XCD-aware workgroup order: the dispatcher deals workgroups to the 8 XCDs
+// round-robin; remapping makes XCD x walk its own contiguous eighth.
+#ifndef ZK_XCD_REMAP
+#define ZK_XCD_REMAP 0
+#endif
+constexpr int kXcds = 8;
+#ifndef ZK_NT_COPY
+#define ZK_NT_COPY 1
+#endif
+// Segment copy: workgroup size, and 16-byte vectors per lane per chunk.
+#ifndef ZK_COPY_BLOCK
+#define ZK_COPY_BLOCK 64
+#endif
+#ifndef ZK_COPY_VPT
+#define ZK_COPY_VPT 1
+#endif
+// Dynamic LDS reserved (unused) per fused-step workgroup: caps how many
+// workgroups share a CU (160 KiB of LDS per CU).
+#ifndef ZK_STEP_LDS
+#define ZK_STEP_LDS 0
+#endif
+constexpr int kStepVpt = ZK_STEP_VPT;
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ uint4 ld_u4(const void *p) {
+    if (NT) {
+        u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+        return make_uint4(v.x, v.y, v.z, v.w);
+    }
+    return *reinterpret_cast<const uint4 *>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ float4 ld_f4(const void *p) {
+    if (NT) {
+        f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+        return make_float4(v.x, v.y, v.z, v.w);
+    }
+    return *reinterpret_cast<const float4 *>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void st_u4(void *p, uint4 v) {
+    if (NT) {
+        u32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+    } else {
+        *reinterpret_cast<uint4 *>(p) = v;
+    }
+}
+
+template <bool NT>
+__device__ __forceinline__ void st_f4(void *p, float4 v) {
+    if (NT) {
+        f32x4_t w = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t *>(p));
+    } else {
+        *reinterpret_cast<float4 *>(p) = v;
+    }
+}
 
 __device__ __forceinline__ float widen_bf16(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
@@ -80,7 +173,7 @@ __device__ __forceinline__ RawVec<GB> load_vec(const void *base, int64_t j);
 template <>
 __device__ __forceinline__ RawVec<true> load_vec<true>(const void *base, int64_t j) {
     RawVec<true> r;
-    r.a = reinterpret_cast<const uint4 *>(base)[j];
+    r.a = ld_u4<ZK_NT_GRAD>(reinterpret_cast<const uint4 *>(base) + j);
     return r;
 }
 
@@ -88,8 +181,8 @@ template <>
 __device__ __forceinline__ RawVec<false> load_vec<false>(const void *base, int64_t j) {
     RawVec<false> r;
     const float4 *p = reinterpret_cast<const float4 *>(base);
-    r.a = p[2 * j];
-    r.b = p[2 * j + 1];
+    r.a = ld_f4<ZK_NT_GRAD>(p + 2 * j);
+    r.b = ld_f4<ZK_NT_GRAD>(p + 2 * j + 1);
     return r;
 }
 
@@ -107,15 +200,16 @@ __device__ __forceinline__ void unpack(const RawVec<false> &r, float (&x)[kVec])
 
 __device__ __forceinline__ void load8(const float *base, int64_t j, float (&x)[kVec]) {
     const float4 *p = reinterpret_cast<const float4 *>(base);
-    float4 a = p[2 * j], b = p[2 * j + 1];
+    float4 a = ld_f4<ZK_NT_STATE>(p + 2 * j), b = ld_f4<ZK_NT_STATE>(p + 2 * j + 1);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+template <bool NT>
 __device__ __forceinline__ void store8(float *base, int64_t j, const float (&x)[kVec]) {
     float4 *p = reinterpret_cast<float4 *>(base);
-    p[2 * j] = make_float4(x[0], x[1], x[2], x[3]);
-    p[2 * j + 1] = make_float4(x[4], x[5], x[6], x[7]);
+    st_f4<NT>(p + 2 * j, make_float4(x[0], x[1], x[2], x[3]));
+    st_f4<NT>(p + 2 * j + 1, make_float4(x[4], x[5], x[6], x[7]));
 }
 
 // Fold one group of up to kGroup replicas into s (rank order). The group's
@@ -148,6 +242,56 @@ __device__ __forceinline__ void fold_group(const Reps<NR> &reps, int q0, int n, 
 // NR > 0 fixes the replica count at compile time (N <= 16 fully unrolled;
 // larger N walks the groups in a loop to bound register use); NR == 0 reads
 // it from `nrep`.
+// One 8-element vector j of the fused step.
+template <int NR, bool GB, bool PB>
+__device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool pow2,
+                                            float *__restrict__ master, float *__restrict__ mom,
+                                            float *__restrict__ var, void *__restrict__ out,
+                                            int64_t j, const StepScalars &sc) {
+    float p[kVec], m[kVec], v[kVec];
+    load8(master, j, p);
+    load8(mom, j, m);
+    load8(var, j, v);
+
+    float s[kVec];
+    if constexpr (NR > 0 && NR <= 2 * kGroup) {
+#pragma unroll
+        for (int q0 = 0; q0 < NR; q0 += kGroup) fold_group<NR, GB>(reps, q0, NR, j, s);
+    } else {
+#pragma unroll 1
+        for (int q0 = 0; q0 < n; q0 += kGroup) fold_group<NR, GB>(reps, q0, n, j, s);
+    }
+
+    float g[kVec];
+    if (pow2) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;   // exact scaling
+    } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
+    }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
+
+    store8<ZK_NT_STATE || ZK_NT_STATE_ST>(master, j, p);
+    store8<ZK_NT_STATE || ZK_NT_STATE_ST>(mom, j, m);
+    store8<ZK_NT_STATE || ZK_NT_STATE_ST>(var, j, v);
+    if (PB) {
+        uint4 o;
+        o.x = round_bf16(p[0]) | (round_bf16(p[1]) << 16);
+        o.y = round_bf16(p[2]) | (round_bf16(p[3]) << 16);
+        o.z = round_bf16(p[4]) | (round_bf16(p[5]) << 16);
+        o.w = round_bf16(p[6]) | (round_bf16(p[7]) << 16);
+        st_u4<ZK_NT_OUT>(reinterpret_cast<uint4 *>(out) + j, o);
+    } else {
+        store8<ZK_NT_OUT>(reinterpret_cast<float *>(out), j, p);
+    }
+}
+
+// Vector path: every stream 16-byte aligned; lane handles elements
+// [8j, 8j+8) of vector j. NR > 0 fixes the replica count at compile time
+// (N <= 16 fully unrolled; larger N walks the groups in a loop to bound
+// register use); NR == 0 reads it from `nrep`.
 template <int NR, bool GB, bool PB>
 __global__ void __launch_bounds__(kBlock)
 step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
@@ -156,46 +300,30 @@ step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
     const int n = NR > 0 ? NR : nrep;
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < nvec; j += stride) {
-        float p[kVec], m[kVec], v[kVec];
-        load8(master, j, p);
-        load8(mom, j, m);
-        load8(var, j, v);
-
-        float s[kVec];
-        if constexpr (NR > 0 && NR <= 2 * kGroup) {
-#pragma unroll
-            for (int q0 = 0; q0 < NR; q0 += kGroup) fold_group<NR, GB>(reps, q0, NR, j, s);
-        } else {
-#pragma unroll 1
-            for (int q0 = 0; q0 < n; q0 += kGroup) fold_group<NR, GB>(reps, q0, n, j, s);
+    if constexpr (kStepVpt > 0) {
+        int64_t bid = blockIdx.x;
+        if (ZK_XCD_REMAP) {      // grid is a multiple of kXcds
+            const int64_t per = gridDim.x / kXcds;
+            bid = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
         }
-
-        float g[kVec];
-        if (pow2) {
+        const int64_t base = bid * (kBlock * kStepVpt) + threadIdx.x;
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;   // exact scaling
-        } else {
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
+        for (int k = 0; k < kStepVpt; ++k) {
+            const int64_t j = base + (int64_t)k * kBlock;
+            if (j < nvec) step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
         }
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
-
-        store8(master, j, p);
-        store8(mom, j, m);
-        store8(var, j, v);
-        if (PB) {
-            uint4 o;
-            o.x = round_bf16(p[0]) | (round_bf16(p[1]) << 16);
-            o.y = round_bf16(p[2]) | (round_bf16(p[3]) << 16);
-            o.z = round_bf16(p[4]) | (round_bf16(p[5]) << 16);
-            o.w = round_bf16(p[6]) | (round_bf16(p[7]) << 16);
-            reinterpret_cast<uint4 *>(out)[j] = o;
-        } else {
-            store8(reinterpret_cast<float *>(out), j, p);
-        }
+    } else if constexpr (kStepVpt < 0) {
+        const int64_t G = gridDim.x;
+        int64_t per = (nvec + G - 1) / G;
+        per = (per + kBlock - 1) / kBlock * kBlock;
+        const int64_t beg = (int64_t)blockIdx.x * per;
+        const int64_t end = beg + per < nvec ? beg + per : nvec;
+        for (int64_t j = beg + threadIdx.x; j < end; j += kBlock)
+            step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
+    } else {
+        const int64_t stride = (int64_t)gridDim.x * kBlock;
+        for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < nvec; j += stride)
+            step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
     }
 }
 
@@ -233,11 +361,20 @@ template <int NR, bool GB, bool PB>
 hipError_t launch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
     Reps<NR> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
-    int64_t want = (nvec + kBlock - 1) / kBlock;
-    int64_t cap = (int64_t)a.num_cus * 8;
-    int grid = (int)(want < cap ? want : cap);
-    hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB>), dim3(grid), dim3(kBlock), 0,
-                       stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, a.sc);
+    int64_t grid;
+    if (kStepVpt > 0) {
+        const int64_t per_block = (int64_t)kBlock * kStepVpt;
+        grid = (nvec + per_block - 1) / per_block;
+        if (ZK_XCD_REMAP) grid = (grid + kXcds - 1) / kXcds * kXcds;
+        // a dispatch holds at most 2^32-1 work-items
+        if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
+    } else {
+        const int64_t want = (nvec + kBlock - 1) / kBlock;
+        const int64_t cap = (int64_t)a.num_cus * (kStepVpt < 0 ? ZK_STEP_BPC : 8);
+        grid = want < cap ? want : cap;
+    }
+    hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB>), dim3((unsigned)grid), dim3(kBlock),
+                       ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, a.sc);
     return hipGetLastError();
 }
 
@@ -284,7 +421,8 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
 // ------------------------------------------------------------ segment copy
 
 constexpr int kSegBatch = 64;                 // segments per launch
-constexpr int64_t kChunk = 65536;             // bytes per workgroup
+constexpr int kCopyBlock = ZK_COPY_BLOCK;
+constexpr int64_t kChunk = (int64_t)kCopyBlock * 16 * ZK_COPY_VPT;   // bytes per workgroup
 
 struct SegBatch {
     const char *src[kSegBatch];
@@ -298,7 +436,7 @@ struct SegBatch {
 template <typename T>
 __device__ __forceinline__ void copy_elems(const char *src, char *dst, int64_t nbytes) {
     const int64_t n = nbytes / (int64_t)sizeof(T);
-    for (int64_t k = threadIdx.x; k < n; k += kBlock) {
+    for (int64_t k = threadIdx.x; k < n; k += kCopyBlock) {
         T x = src ? reinterpret_cast<const T *>(src)[k] : T(0);
         reinterpret_cast<T *>(dst)[k] = x;
     }
@@ -313,7 +451,7 @@ __device__ __forceinline__ void copy_elems_any(const char *src, char *dst, int64
 // destination with the same offset within 16 bytes take 16-byte vectors
 // after a short element-wise head; otherwise the chunk is copied element by
 // element (consecutive lanes, consecutive elements).
-__global__ void __launch_bounds__(kBlock) copy_segments_kernel(SegBatch b) {
+__global__ void __launch_bounds__(kCopyBlock) copy_segments_kernel(SegBatch b) {
     const int64_t w = blockIdx.x;
     int lo = 0, hi = b.nseg - 1;              // last segment with blk0 <= w
     while (lo < hi) {
@@ -343,17 +481,19 @@ __global__ void __launch_bounds__(kBlock) copy_segments_kernel(SegBatch b) {
     uint4 *d4 = reinterpret_cast<uint4 *>(dst + head);
     int64_t k = threadIdx.x;
     if (s4) {
-        for (; k + 3 * kBlock < nv; k += 4 * kBlock) {
-            uint4 x0 = s4[k], x1 = s4[k + kBlock], x2 = s4[k + 2 * kBlock], x3 = s4[k + 3 * kBlock];
-            d4[k] = x0;
-            d4[k + kBlock] = x1;
-            d4[k + 2 * kBlock] = x2;
-            d4[k + 3 * kBlock] = x3;
+        for (; k + 3 * kCopyBlock < nv; k += 4 * kCopyBlock) {
+            uint4 x0 = ld_u4<ZK_NT_COPY>(s4 + k), x1 = ld_u4<ZK_NT_COPY>(s4 + k + kCopyBlock);
+            uint4 x2 = ld_u4<ZK_NT_COPY>(s4 + k + 2 * kCopyBlock);
+            uint4 x3 = ld_u4<ZK_NT_COPY>(s4 + k + 3 * kCopyBlock);
+            st_u4<ZK_NT_COPY>(d4 + k, x0);
+            st_u4<ZK_NT_COPY>(d4 + k + kCopyBlock, x1);
+            st_u4<ZK_NT_COPY>(d4 + k + 2 * kCopyBlock, x2);
+            st_u4<ZK_NT_COPY>(d4 + k + 3 * kCopyBlock, x3);
         }
-        for (; k < nv; k += kBlock) d4[k] = s4[k];
+        for (; k < nv; k += kCopyBlock) st_u4<ZK_NT_COPY>(d4 + k, ld_u4<ZK_NT_COPY>(s4 + k));
     } else {
         const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        for (; k < nv; k += kBlock) d4[k] = z;
+        for (; k < nv; k += kCopyBlock) st_u4<ZK_NT_COPY>(d4 + k, z);
     }
     const int64_t done = head + nv * 16;
     copy_elems_any(src ? src + done : nullptr, dst + done, len - done, b.esize);
@@ -385,27 +525,37 @@ hipError_t launch_step(const StepArgs &a, hipStream_t stream) {
 }
 
 hipError_t launch_copy_segments(const Segment *segs, int nseg, int esize, hipStream_t stream) {
+    // A dispatch holds at most 2^32-1 work-items; long segments are cut into
+    // pieces at multiples of the chunk size (which keeps every piece's
+    // source/destination alignment relation) and batched under that limit.
+    const int64_t max_blocks = (int64_t)(0xFFFFFFFFu / kCopyBlock);
+    const int64_t max_piece = kChunk * (max_blocks / 4);
     int i = 0;
+    int64_t done = 0;                          // bytes of segs[i] already issued
     while (i < nseg) {
         SegBatch b;
         b.esize = esize;
         b.nseg = 0;
         int64_t blocks = 0;
         while (i < nseg && b.nseg < kSegBatch) {
-            const Segment &s = segs[i++];
-            if (s.nbytes <= 0) continue;
-            b.src[b.nseg] = static_cast<const char *>(s.src);
-            b.dst[b.nseg] = static_cast<char *>(s.dst);
-            b.nbytes[b.nseg] = s.nbytes;
+            const Segment &s = segs[i];
+            int64_t len = s.nbytes - done;
+            if (len <= 0) { ++i; done = 0; continue; }
+            if (len > max_piece) len = max_piece;
+            const int64_t nb = (len + kChunk - 1) / kChunk;
+            if (blocks + nb > max_blocks) break;
+            b.src[b.nseg] = s.src ? static_cast<const char *>(s.src) + done : nullptr;
+            b.dst[b.nseg] = static_cast<char *>(s.dst) + done;
+            b.nbytes[b.nseg] = len;
             b.blk0[b.nseg] = blocks;
-            blocks += (s.nbytes + kChunk - 1) / kChunk;
+            blocks += nb;
             b.nseg++;
+            done += len;
+            if (done >= s.nbytes) { ++i; done = 0; }
         }
         if (b.nseg == 0) continue;
         b.blk0[b.nseg] = blocks;
-        // a dispatch holds at most 2^32-1 work-items: 2^24 workgroups of 64 KiB
-        if (blocks > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(copy_segments_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+        hipLaunchKernelGGL(copy_segments_kernel, dim3((unsigned)blocks), dim3(kCopyBlock), 0,
                            stream, b);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
