@@ -50,6 +50,10 @@ constexpr int kGroup = 8;            // replicas loaded together
 #ifndef ZK_STEP_BPC
 #define ZK_STEP_BPC 8
 #endif
+// With ZK_STEP_VPT=2: issue both vectors' loads before computing either.
+#ifndef ZK_STEP_PAIR
+#define ZK_STEP_PAIR 0
+#endif
 // Non-temporal (streaming) hints: every stream is touched once per step.
 #ifndef ZK_NT_GRAD
 #define ZK_NT_GRAD 1
@@ -81,9 +85,11 @@ constexpr int kXcds = 8;
 #define ZK_COPY_VPT 1
 #endif
 // Dynamic LDS reserved (unused) per fused-step workgroup: caps how many
-// workgroups share a CU (160 KiB of LDS per CU).
+// workgroups share a CU (160 KiB of LDS per CU). The default, all of it,
+// keeps one 512-lane workgroup (8 waves) per CU: measured best, since more
+// waves put more streams' requests in flight than the HBM serves well.
 #ifndef ZK_STEP_LDS
-#define ZK_STEP_LDS 0
+#define ZK_STEP_LDS 163840
 #endif
 constexpr int kStepVpt = ZK_STEP_VPT;
 
@@ -237,11 +243,6 @@ __device__ __forceinline__ void fold_group(const Reps<NR> &reps, int q0, int n, 
     }
 }
 
-// Vector path: every stream 16-byte aligned; lane handles elements
-// [8j, 8j+8) of vector j, vectors strided over the whole grid.
-// NR > 0 fixes the replica count at compile time (N <= 16 fully unrolled;
-// larger N walks the groups in a loop to bound register use); NR == 0 reads
-// it from `nrep`.
 // One 8-element vector j of the fused step.
 template <int NR, bool GB, bool PB>
 __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool pow2,
@@ -288,6 +289,58 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
     }
 }
 
+// Two vectors per lane with both vectors' loads issued before either is
+// computed (more bytes in flight per wave).
+template <int NR, bool GB, bool PB>
+__device__ __forceinline__ void step_vector_pair(const Reps<NR> &reps, bool pow2,
+                                                 float *__restrict__ master,
+                                                 float *__restrict__ mom,
+                                                 float *__restrict__ var,
+                                                 void *__restrict__ out, int64_t j0, int64_t j1,
+                                                 const StepScalars &sc) {
+    static_assert(NR > 0 && NR <= kGroup, "pair path: compile-time N <= 8");
+    float p[2][kVec], m[2][kVec], v[2][kVec];
+    RawVec<GB> raw[2][NR];
+    const int64_t js[2] = {j0, j1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        load8(master, js[h], p[h]);
+        load8(mom, js[h], m[h]);
+        load8(var, js[h], v[h]);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) raw[h][k] = load_vec<GB>(reps.p[k], js[h]);
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float s[kVec];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            float x[kVec];
+            unpack(raw[h][k], x);
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) s[e] = k == 0 ? x[e] : s[e] + x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+            const float g = pow2 ? s[e] * sc.inv_n : s[e] / sc.nf;
+            adam_update(g, p[h][e], m[h][e], v[h][e], sc);
+        }
+        store8<ZK_NT_STATE || ZK_NT_STATE_ST>(master, js[h], p[h]);
+        store8<ZK_NT_STATE || ZK_NT_STATE_ST>(mom, js[h], m[h]);
+        store8<ZK_NT_STATE || ZK_NT_STATE_ST>(var, js[h], v[h]);
+        if (PB) {
+            uint4 o;
+            o.x = round_bf16(p[h][0]) | (round_bf16(p[h][1]) << 16);
+            o.y = round_bf16(p[h][2]) | (round_bf16(p[h][3]) << 16);
+            o.z = round_bf16(p[h][4]) | (round_bf16(p[h][5]) << 16);
+            o.w = round_bf16(p[h][6]) | (round_bf16(p[h][7]) << 16);
+            st_u4<ZK_NT_OUT>(reinterpret_cast<uint4 *>(out) + js[h], o);
+        } else {
+            store8<ZK_NT_OUT>(reinterpret_cast<float *>(out), js[h], p[h]);
+        }
+    }
+}
+
 // Vector path: every stream 16-byte aligned; lane handles elements
 // [8j, 8j+8) of vector j. NR > 0 fixes the replica count at compile time
 // (N <= 16 fully unrolled; larger N walks the groups in a loop to bound
@@ -300,7 +353,15 @@ step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
     const int n = NR > 0 ? NR : nrep;
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
-    if constexpr (kStepVpt > 0) {
+    if constexpr (kStepVpt == 2 && ZK_STEP_PAIR && NR > 0 && NR <= kGroup) {
+        const int64_t j0 = (int64_t)blockIdx.x * (kBlock * 2) + threadIdx.x;
+        const int64_t j1 = j0 + kBlock;
+        if (j1 < nvec) {
+            step_vector_pair<NR, GB, PB>(reps, pow2, master, mom, var, out, j0, j1, sc);
+        } else if (j0 < nvec) {
+            step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j0, sc);
+        }
+    } else if constexpr (kStepVpt > 0) {
         int64_t bid = blockIdx.x;
         if (ZK_XCD_REMAP) {      // grid is a multiple of kXcds
             const int64_t per = gridDim.x / kXcds;
