@@ -103,6 +103,71 @@ def cpu_baseline(window: int, min_seconds: float):
                         f"over {WORLD} replicas, {el:.1f} s wall"))
 
 
+def _time_ms(fn, reps=5):
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def bucketed_extras(st, reps, out, t0, sizes=(1 << 22, 1 << 24, 1 << 26), nstreams=2):
+    """The same step applied bucket by bucket (zero_step_range) on
+    `nstreams` streams: time of a whole shard's worth of buckets."""
+    S = st.shard
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
+    cur = torch.cuda.current_stream()
+    res = {}
+    t = [t0]
+
+    def run(bucket):
+        for i, b0 in enumerate(range(0, S, bucket)):
+            cnt = min(bucket, S - b0)
+            s = streams[i % nstreams]
+            s.wait_stream(cur)
+            st.step_range(b0, cnt, [r[b0:] for r in reps], t[0], out, grad_offset=0,
+                          param_offset=b0, stream=s)
+        for s in streams:
+            cur.wait_stream(s)
+        t[0] += 1
+
+    for bucket in sizes:
+        ms = _time_ms(lambda: run(bucket), reps=3)
+        res[str(bucket)] = {"buckets": (S + bucket - 1) // bucket, "ms": ms,
+                            "gbps": step_bytes_per_elem(WORLD) * S / (ms * 1e-3) / 1e9}
+    return res
+
+
+def list_extras(dev):
+    """Multi-tensor flatten and unflatten on the Llama-7B-shaped list
+    (291 tensors, 6,738,415,616 bf16 elements)."""
+    shapes = synth.llama_shapes(32, 4096, 11008)
+    numel = synth.numel_of(shapes)
+    st = zero.ShardState(numel, WORLD, 0, LR, BETAS, EPS)
+    storage = torch.empty(numel, dtype=torch.bfloat16, device=dev)
+    synth.fill_gaussian(storage, 1e-3, 11)
+    tensors = synth.split_views(storage, shapes)
+    flat = torch.empty(st.padded, dtype=torch.bfloat16, device=dev)
+    ms_f = _time_ms(lambda: st.flatten(tensors, flat))
+    ok = torch.equal(flat[:numel].view(torch.int16), storage.view(torch.int16))
+    dst_storage = torch.empty(numel, dtype=torch.bfloat16, device=dev)
+    dsts = synth.split_views(dst_storage, shapes)
+    ms_u = _time_ms(lambda: st.unflatten(flat, dsts))
+    ok = ok and torch.equal(dst_storage.view(torch.int16), storage.view(torch.int16))
+    res = {"tensors": len(shapes), "numel": numel,
+           "flatten": {"ms": ms_f, "gbps": (2 * numel + 2 * st.padded) / (ms_f * 1e-3) / 1e9},
+           "unflatten": {"ms": ms_u, "gbps": 4 * numel / (ms_u * 1e-3) / 1e9},
+           "bit_exact": bool(ok)}
+    del storage, flat, dst_storage, tensors, dsts
+    st.close()
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_ceiling(nbytes: int, reps: int = 5):
     """torch device-to-device copy as a plain-copy context figure."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -131,6 +196,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the plain-copy context measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the bucketed-step and tensor-list measurements")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one rank's shard step on one GPU; runs on more than one "
@@ -199,6 +266,11 @@ def main():
     # the step must have produced finite, changing parameters
     assert torch.isfinite(params_full[:S].float()).all().item()
 
+    extras = {}
+    if not args.no_extras:
+        log("bucketed step")
+        extras["bucketed_step_2_streams"] = bucketed_extras(st, reps, params_full, n_total + 1)
+
     del own_grad, own_flat, peers, reps, params_full
     st.close()
     torch.cuda.empty_cache()
@@ -206,6 +278,9 @@ def main():
     context = {}
     if not args.no_context:
         context["torch_copy_gbps"] = round(copy_ceiling(8 << 30), 1)
+    if not args.no_extras:
+        log("tensor-list flatten/unflatten")
+        extras["llama7b_list"] = list_extras(dev)
 
     result = {
         "metric": "sharded Adam step: elements/s and achieved HBM GB/s (% of peak), 7B N=8",
@@ -237,6 +312,7 @@ def main():
                      "traffic": traffic,
                      "kernel": "fused reduce+Adam+bf16 step (step_vec_kernel<8,bf16,bf16>)"},
         "context": context,
+        "extras": extras,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -60,6 +60,8 @@ def lib():
     L.zero_flatten.argtypes = [vp, vp, vp, i32, ctypes.c_int, vp, vp]
     L.zero_unflatten.argtypes = [vp, vp, i32, vp, ctypes.c_int, vp, vp]
     L.zero_step.argtypes = [vp, vp, i32, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, vp]
+    L.zero_step_range.argtypes = [vp, i64, i64, vp, i32, ctypes.c_int, i64, vp, ctypes.c_int,
+                                  i64, i64, vp]
     L.zero_get_state.argtypes = [vp, vp, vp, vp, vp]
     L.zero_set_state.argtypes = [vp, vp, vp, vp, vp]
     L.zero_state_bytes.argtypes = [i32, dbl, dbl, ctypes.POINTER(dbl)]
@@ -236,6 +238,47 @@ class ShardState:
         _check(lib().zero_step(self._h, ptrs, len(replicas), _dtype_code(gdt), go,
                                param_out.data_ptr(), _dtype_code(param_out.dtype), po,
                                int(t), _stream_handle(stream)))
+
+    def step_range(self, shard_begin: int, count: int, replicas: Sequence[torch.Tensor],
+                   t: int, param_out: torch.Tensor, grad_offset: int = 0,
+                   param_offset: int = 0, stream=None):
+        """The step on shard elements [shard_begin, shard_begin+count):
+        replicas[q][grad_offset + i] feeds element shard_begin + i, which is
+        written to param_out[param_offset + i]. Disjoint ranges on different
+        streams may run concurrently."""
+        if len(replicas) != self.world:
+            raise ValueError(f"need {self.world} replicas, got {len(replicas)}")
+        if shard_begin < 0 or count < 0 or shard_begin + count > self.shard:
+            raise ValueError(f"range [{shard_begin}, {shard_begin + count}) outside the shard")
+        gdt = replicas[0].dtype
+        for q, r in enumerate(replicas):
+            self._dev(r, f"replicas[{q}]")
+            if r.dtype != gdt:
+                raise TypeError("replicas must share one dtype")
+            if r.numel() < grad_offset + count:
+                raise ValueError(f"replicas[{q}] has {r.numel()} elements, need {grad_offset + count}")
+        self._dev(param_out, "param_out")
+        if param_out.numel() < param_offset + count:
+            raise ValueError(f"param_out has {param_out.numel()} elements, need {param_offset + count}")
+        ptrs = _ptr_array([r.data_ptr() for r in replicas])
+        _check(lib().zero_step_range(self._h, int(shard_begin), int(count), ptrs, len(replicas),
+                                     _dtype_code(gdt), int(grad_offset), param_out.data_ptr(),
+                                     _dtype_code(param_out.dtype), int(param_offset), int(t),
+                                     _stream_handle(stream)))
+
+    def bucket_ranges(self, bucket_bounds: Sequence[int]) -> List[Tuple[int, int, int, int]]:
+        """For gradient buckets given as flat-vector boundaries
+        [b0=0, b1, ..., bk=padded], the part of each bucket this rank owns:
+        (bucket index, shard_begin, count, offset of that part inside the
+        bucket). Buckets that miss this rank's slice are left out."""
+        out = []
+        lo, hi = self.lo, self.lo + self.shard
+        for k in range(len(bucket_bounds) - 1):
+            a, b = int(bucket_bounds[k]), int(bucket_bounds[k + 1])
+            s, e = max(a, lo), min(b, hi)
+            if s < e:
+                out.append((k, s - lo, e - s, s - a))
+        return out
 
     def get_state(self, stream=None) -> List[torch.Tensor]:
         """Fresh fp32 copies of (master, m, v)."""

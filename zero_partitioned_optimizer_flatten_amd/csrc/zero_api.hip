@@ -293,10 +293,14 @@ int zero_unflatten(const zero_ctx *c, const void *flat, int32_t ntensors, const 
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "unflatten launch");
 }
 
-int zero_step(zero_ctx *c, const void *const *grads, int32_t n_replicas, zero_dtype grad_dtype,
-              int64_t grad_offset, void *param_out, zero_dtype param_dtype, int64_t param_offset,
-              int64_t t, hipStream_t stream) {
+static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *const *grads,
+                       int32_t n_replicas, zero_dtype grad_dtype, int64_t grad_offset,
+                       void *param_out, zero_dtype param_dtype, int64_t param_offset, int64_t t,
+                       hipStream_t stream) {
     if (!c) return fail(ZERO_EINVAL, "null context");
+    if (begin < 0 || count < 0 || begin > c->shard - count)
+        return fail(ZERO_EINVAL, "range [%lld, %lld) outside the shard of %lld elements",
+                    (long long)begin, (long long)(begin + count), (long long)c->shard);
     if (n_replicas != c->world)
         return fail(ZERO_EINVAL, "n_replicas (%d) must equal world (%d)", n_replicas, c->world);
     if (t < 1) return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
@@ -311,12 +315,13 @@ int zero_step(zero_ctx *c, const void *const *grads, int32_t n_replicas, zero_dt
         if (!grads[q]) return fail(ZERO_EINVAL, "replica %d is null", q);
         if ((uintptr_t)grads[q] % ge) return fail(ZERO_EINVAL, "replica %d misaligned", q);
         slices[q] = (const char *)grads[q] + (size_t)grad_offset * ge;
-        int rc = check_range(grads[q], (grad_offset + c->shard) * (int64_t)ge, "gradient replica");
+        int rc = check_range(grads[q], (grad_offset + count) * (int64_t)ge, "gradient replica");
         if (rc) return rc;
     }
     if ((uintptr_t)param_out % pe) return fail(ZERO_EINVAL, "parameter output misaligned");
-    int rc = check_range(param_out, (param_offset + c->shard) * (int64_t)pe, "parameter output");
+    int rc = check_range(param_out, (param_offset + count) * (int64_t)pe, "parameter output");
     if (rc) return rc;
+    if (count == 0) return ZERO_OK;
     DeviceGuard g(c->device);
     if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
 
@@ -324,16 +329,32 @@ int zero_step(zero_ctx *c, const void *const *grads, int32_t n_replicas, zero_dt
     a.grads = slices;
     a.n = n_replicas;
     a.grad_bf16 = grad_dtype == ZERO_BF16;
-    a.master = c->master;
-    a.m = c->m;
-    a.v = c->v;
+    a.master = c->master + begin;
+    a.m = c->m + begin;
+    a.v = c->v + begin;
     a.out = (char *)param_out + (size_t)param_offset * pe;
     a.out_bf16 = param_dtype == ZERO_BF16;
-    a.shard = c->shard;
+    a.shard = count;
     a.sc = make_scalars(c, t);
     a.num_cus = c->num_cus;
     hipError_t e = zk::launch_step(a, stream);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "step launch");
+}
+
+int zero_step(zero_ctx *c, const void *const *grads, int32_t n_replicas, zero_dtype grad_dtype,
+              int64_t grad_offset, void *param_out, zero_dtype param_dtype, int64_t param_offset,
+              int64_t t, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    return step_common(c, 0, c->shard, grads, n_replicas, grad_dtype, grad_offset, param_out,
+                       param_dtype, param_offset, t, stream);
+}
+
+int zero_step_range(zero_ctx *c, int64_t shard_begin, int64_t count, const void *const *grads,
+                    int32_t n_replicas, zero_dtype grad_dtype, int64_t grad_offset,
+                    void *param_out, zero_dtype param_dtype, int64_t param_offset, int64_t t,
+                    hipStream_t stream) {
+    return step_common(c, shard_begin, count, grads, n_replicas, grad_dtype, grad_offset,
+                       param_out, param_dtype, param_offset, t, stream);
 }
 
 static int copy_state(const zero_ctx *c, const float *const src[3], float *const dst[3],
