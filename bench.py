@@ -168,6 +168,41 @@ def list_extras(dev):
     return res
 
 
+def fsdp_extras(dev, steps=5):
+    """Per-parameter (dim-0) layout: the fused step over this rank's row
+    shards of the Llama-7B-shaped list (291 parameters), N = 8, rank 0.
+    Replica gradients are full-size tensors; only this rank's rows are read."""
+    shapes = synth.llama_shapes(32, 4096, 11008)
+    st = zero.FsdpShardState(shapes, WORLD, 0, LR, BETAS, EPS)
+    local = sum(st.local_numel(k) for k in range(len(shapes)))
+    params = [torch.empty(s, dtype=torch.float32, device=dev) for s in shapes]
+    for k, p in enumerate(params):
+        f, r, _ = st.local[k]
+        synth.fill_gaussian(p.view(p.shape[0], -1)[f:f + r], synth.PARAM_STD, k)
+    st.load_master(params)
+    del params
+    grads = [[torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+             for _ in range(WORLD)]
+    for q in range(WORLD):
+        for k, g in enumerate(grads[q]):
+            f, r, _ = st.local[k]
+            synth.fill_gaussian(g.view(g.shape[0], -1)[f:f + r], 1e-3, 1000 * q + k)
+    outs = [torch.empty(max(1, st.local_numel(k)), dtype=torch.bfloat16, device=dev)
+            for k in range(len(shapes))]
+    t = [1]
+
+    def one():
+        st.step(grads, t[0], outs)
+        t[0] += 1
+    ms = _time_ms(one, reps=steps)
+    res = {"tensors": len(shapes), "local_elements": local, "ms": ms,
+           "gbps": step_bytes_per_elem(WORLD) * local / (ms * 1e-3) / 1e9}
+    del grads, outs
+    st.close()
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_ceiling(nbytes: int, reps: int = 5):
     """torch device-to-device copy as a plain-copy context figure."""
     a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
@@ -281,6 +316,8 @@ def main():
     if not args.no_extras:
         log("tensor-list flatten/unflatten")
         extras["llama7b_list"] = list_extras(dev)
+        log("per-parameter (dim-0) layout step")
+        extras["fsdp_llama7b_n8_rank0"] = fsdp_extras(dev)
 
     result = {
         "metric": "sharded Adam step: elements/s and achieved HBM GB/s (% of peak), 7B N=8",

@@ -162,6 +162,61 @@ int zero_step_range(zero_ctx *ctx, int64_t shard_begin, int64_t count,
                     void *param_out, zero_dtype param_dtype,
                     int64_t param_offset, int64_t t, hipStream_t stream);
 
+/* ---- Per-parameter (dim-0) layout ------------------------------------
+ * [ZeRO and FSDP], section "ZeRO-3 and FSDP": FSDP2 keeps every parameter
+ * as a tensor partitioned along dimension 0, and the optimizer acts on the
+ * local pieces, so its state is partitioned the same way. Rank r holds
+ * rows [r*c, min((r+1)*c, dim0)) of a parameter with dim0 rows, where
+ * c = ceil(dim0 / world); trailing ranks may hold fewer rows or none. */
+
+/* Largest world the per-parameter layout accepts. */
+#define ZERO_FSDP_MAX_WORLD 16
+
+/* This rank's rows of a dim0-row parameter (host only). Out-pointers may be
+ * NULL. EINVAL unless dim0 >= 0, world >= 1, 0 <= rank < world. */
+int zero_dim0_split(int64_t dim0, int32_t world, int32_t rank,
+                    int64_t *first_row, int64_t *rows);
+
+/* Context for `ntensors` parameters, parameter k having dim0[k] rows of
+ * row_numel[k] elements (row-major). The library allocates fp32 master, m
+ * and v for this rank's rows of every parameter, concatenated in order with
+ * each piece starting on a multiple of 8 elements, all zero.
+ * zero_shard_info reports the state length as `shard` (lo = 0).
+ * zero_get_state / zero_set_state / zero_set_lr / zero_destroy apply;
+ * the flat-layout calls (zero_load_master, zero_flatten, zero_unflatten,
+ * zero_step, zero_step_range) return EINVAL on this context.
+ * EINVAL: ntensors < 1, a dim0 < 0 or row_numel < 1, bad rank/world or
+ * hyperparameters (as zero_shard_init). EUNSUPPORTED: world >
+ * ZERO_FSDP_MAX_WORLD. ENOMEM / EHIP as zero_shard_init. Synchronous. */
+int zero_fsdp_init(int32_t ntensors, const int64_t *dim0,
+                   const int64_t *row_numel, int32_t world, int32_t rank,
+                   double lr, double beta1, double beta2, double eps,
+                   zero_ctx **out);
+
+/* Parameter k's local rows and the offset of its piece in master/m/v. */
+int zero_fsdp_local(const zero_ctx *ctx, int32_t k, int64_t *first_row,
+                    int64_t *rows, int64_t *state_offset);
+
+/* master = fp32(this rank's rows of each full parameter), m = v = 0.
+ * params: host array of ntensors device pointers to the full parameters of
+ * `dtype` (NULL allowed for parameters of which this rank holds no rows). */
+int zero_fsdp_load_master(zero_ctx *ctx, const void *const *params,
+                          zero_dtype dtype, hipStream_t stream);
+
+/* One step on every local piece, with the arithmetic of zero_step: for
+ * each parameter k and each of its local elements, the gradient is the
+ * mean over replicas q (in rank order) of replica q's full gradient of k
+ * at that element; the updated master is written to params_out[k] (this
+ * rank's rows only, bf16 or fp32). grads: host array of n_replicas *
+ * ntensors device pointers, replica-major (grads[q * ntensors + k] is
+ * replica q's full gradient of parameter k). params_out: host array of
+ * ntensors device pointers (NULL allowed where this rank holds no rows).
+ * EINVAL: not a per-parameter context, n_replicas != world, t < 1, null or
+ * misaligned pointers, ranges past their allocations. */
+int zero_fsdp_step(zero_ctx *ctx, const void *const *grads, int32_t n_replicas,
+                   zero_dtype grad_dtype, void *const *params_out,
+                   zero_dtype param_dtype, int64_t t, hipStream_t stream);
+
 /* Copy the fp32 state out of / into the context (checkpoint and resume).
  * master, m, v: device pointers to `shard` floats each; any may be NULL to
  * skip that buffer. Stream-ordered device-to-device copies. */

@@ -52,6 +52,7 @@ def load(path: str):
     i64, i32, vp, dbl = (ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                          ctypes.c_double)
     L.oracle_geometry.argtypes = [i64, i64, i64, vp]
+    L.oracle_dim0_split.argtypes = [i64, i64, i64, vp]
     L.oracle_stage_bytes.argtypes = [ctypes.c_int, dbl, dbl]
     L.oracle_stage_bytes.restype = dbl
     L.oracle_state_bytes.argtypes = [i64]
@@ -113,6 +114,13 @@ def geometry(numel: int, world: int, rank: int) -> dict:
     _check(lib().oracle_geometry(numel, world, rank, _ptr(out)), "geometry")
     return dict(shard=int(out[0]), lo=int(out[1]), padded=int(out[2]),
                 pad=int(out[3]), valid=int(out[4]))
+
+
+def dim0_split(d0: int, world: int, rank: int):
+    """(first row, rows) of this rank's dim-0 shard of a parameter."""
+    out = np.zeros(2, dtype=np.int64)
+    _check(lib().oracle_dim0_split(d0, world, rank, _ptr(out)), "dim0_split")
+    return int(out[0]), int(out[1])
 
 
 def stage_bytes(stage: int, psi: float, n: float) -> float:
@@ -270,3 +278,50 @@ class ShardOracle:
                                        _ptr(self.v), self.shard, _ptr(sc),
                                        _ptr(out), _is_bf16(out), oo),
                "shard_step")
+
+
+class FsdpShardOracle:
+    """One rank of the per-parameter (FSDP2-style) layout: each parameter is
+    split along dim 0 (dim0_split) and the rank keeps fp32 master/m/v for
+    its rows of every parameter. The update of each local shard is the same
+    elementwise step as ShardOracle's, fed by the mean over the N replicas
+    of that parameter's gradient rows."""
+
+    def __init__(self, shapes, world, rank, lr, betas=(0.9, 0.999), eps=1e-8):
+        self.shapes = [tuple(s) for s in shapes]
+        self.world, self.rank = world, rank
+        self.rows = []
+        self.parts = []
+        for shp in self.shapes:
+            d0 = shp[0] if shp else 1
+            row = int(np.prod(shp[1:])) if len(shp) > 1 else 1
+            first, nrows = dim0_split(d0, world, rank)
+            self.rows.append((first, nrows, row))
+            self.parts.append(ShardOracle(max(1, nrows * row), 1, 0, lr, betas, eps,
+                                          n_replicas=world) if nrows * row > 0 else None)
+
+    def local_numels(self):
+        return [n * r for (_, n, r) in self.rows]
+
+    def _local(self, full: np.ndarray, k: int) -> np.ndarray:
+        first, nrows, row = self.rows[k]
+        return np.ascontiguousarray(full.reshape(-1)[first * row:(first + nrows) * row])
+
+    def load_master(self, params_full):
+        for k, p in enumerate(params_full):
+            if self.parts[k] is not None:
+                self.parts[k].load_master(self._local(p, k))
+
+    def step(self, replica_grads, t, outs):
+        """replica_grads[q][k]: replica q's full gradient of parameter k;
+        outs[k]: this rank's local shard of parameter k (written)."""
+        for k, part in enumerate(self.parts):
+            if part is None:
+                continue
+            local = [self._local(replica_grads[q][k], k) for q in range(self.world)]
+            part.step(local, t, outs[k], grad_offset=0, out_offset=0)
+
+    def state(self):
+        keys = ("master", "m", "v")
+        return [np.concatenate([getattr(p, key) for p in self.parts if p is not None]
+                               or [np.zeros(0, np.float32)]) for key in keys]

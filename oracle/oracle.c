@@ -68,6 +68,27 @@ int oracle_geometry(int64_t numel, int64_t world, int64_t rank, int64_t *out)
     return ORACLE_OK;
 }
 
+/* -------------------------------------------------- per-parameter dim-0 split
+ * [ZF] section "ZeRO-3 and FSDP": FSDP2 keeps each parameter as a tensor
+ * partitioned along dimension 0. Rank r holds rows [r*c, min((r+1)*c, d0))
+ * with c = ceil(d0 / world); trailing ranks may hold fewer rows or none.
+ * out[0] = first row, out[1] = number of rows.                             */
+int oracle_dim0_split(int64_t d0, int64_t world, int64_t rank, int64_t *out)
+{
+    if (d0 < 0 || world < 1 || rank < 0 || rank >= world || !out)
+        return ORACLE_EINVAL;
+    int64_t c = d0 / world;
+    if (c * world < d0)
+        c += 1;
+    int64_t first = rank * c;
+    if (first > d0) first = d0;
+    int64_t last = first + c;
+    if (last > d0) last = d0;
+    out[0] = first;
+    out[1] = last - first;
+    return ORACLE_OK;
+}
+
 /* ------------------------------------------------------------ stage bytes
  * [ZF] table "The three stages": model-state bytes per card under
  * mixed-precision Adam with psi parameters and data-parallel degree n.

@@ -643,4 +643,56 @@ def check_nonfinite_stays_local():
     assert np.isnan(o.master[10]) and np.isnan(o.master[20])   # inf/inf in the update
 
 
+# ======================================================= dim-0 layout
+
+def check_dim0_split_vs_torch_chunk():
+    """Library routine: torch.chunk along dim 0, with empty chunks for the
+    ranks it leaves out (the way FSDP2 pads its shard list)."""
+    for d0 in range(0, 41):
+        for world in range(1, 10):
+            chunks = torch.chunk(torch.arange(d0), world, dim=0)
+            rows = [int(c.numel()) for c in chunks] + [0] * (world - len(chunks))
+            first = 0
+            for r in range(world):
+                f, n = oracle.dim0_split(d0, world, r)
+                assert n == rows[r], (d0, world, r)
+                if n:
+                    assert f == first, (d0, world, r)
+                first += n
+
+
+def check_dim0_split_page_example():
+    gold = _golden("fsdp2_rows.json")
+    d0 = gold["weight_shape"][0]
+    for r in range(gold["world"]):
+        assert oracle.dim0_split(d0, gold["world"], r)[1] == gold["local_rows"]
+
+
+def check_fsdp_layout_equals_whole_update():
+    """Every rank's dim-0 shards of every parameter, put back in row order,
+    equal the update of whole parameters, bit for bit (ragged shapes,
+    ranks with no rows)."""
+    rng = np.random.default_rng(21)
+    shapes = [(10, 7), (5,), (1, 3), (13, 2, 2), (3, 4)]
+    world = 4
+    params = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    ranks = [oracle.FsdpShardOracle(shapes, world, r, 1e-3) for r in range(world)]
+    for o in ranks:
+        o.load_master(params)
+    whole = [oracle.ShardOracle(int(np.prod(s)), 1, 0, 1e-3, n_replicas=world) for s in shapes]
+    for w, p in zip(whole, params):
+        w.load_master(p.reshape(-1))
+    for t in range(1, 4):
+        grads = [[(rng.standard_normal(s) * 1e-2).astype(np.float32) for s in shapes]
+                 for _ in range(world)]
+        outs = [[np.zeros(n, np.float32) for n in o.local_numels()] for o in ranks]
+        for o, out in zip(ranks, outs):
+            o.step(grads, t, out)
+        for k, w in enumerate(whole):
+            w.step([grads[q][k].reshape(-1) for q in range(world)], t,
+                   np.zeros(w.shard, np.float32), grad_offset=0, out_offset=0)
+            got = np.concatenate([outs[r][k] for r in range(world)])
+            assert got.tobytes() == w.master.tobytes(), (t, k)
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -107,3 +107,12 @@ def test_null_context_calls_are_rejected():
     assert L.zero_get_state(None, None, None, None, None) == zero.ZERO_EINVAL
     assert L.zero_set_lr(None, 1e-3) == zero.ZERO_EINVAL
     L.zero_destroy(None)
+
+
+def test_dim0_split_matches_oracle():
+    for d0 in (0, 1, 5, 10, 255, 256, 32000):
+        for world in (1, 2, 3, 4, 8, 16):
+            for rank in range(world):
+                assert zero.dim0_split(d0, world, rank) == oracle.dim0_split(d0, world, rank)
+    with pytest.raises(zero.ZeroError):
+        zero.dim0_split(-1, 2, 0)

@@ -46,6 +46,8 @@ MUTANTS = [
     ("master_load_ignores_lo", "master[i] = grad_at(flat, is_bf16, lo + i);", "master[i] = grad_at(flat, is_bf16, i);"),
     ("zero2_wrong_term", "case 2: return 2.0 * psi + 14.0 * psi / n;", "case 2: return 2.0 * psi + 12.0 * psi / n;"),
     ("zero1_wrong_term", "case 1: return 4.0 * psi + 12.0 * psi / n;", "case 1: return 4.0 * psi + 14.0 * psi / n;"),
+    ("dim0_floor", "    if (c * world < d0)\n        c += 1;", "    if (c * world < d0)\n        c += 0;"),
+    ("dim0_no_clamp", "    if (first > d0) first = d0;\n", ""),
     ("state_two_tensors", "return 3 * shard * (int64_t)sizeof(float);", "return 2 * shard * (int64_t)sizeof(float);"),
 ]
 

@@ -62,6 +62,11 @@ def lib():
     L.zero_step.argtypes = [vp, vp, i32, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, vp]
     L.zero_step_range.argtypes = [vp, i64, i64, vp, i32, ctypes.c_int, i64, vp, ctypes.c_int,
                                   i64, i64, vp]
+    L.zero_dim0_split.argtypes = [i64, i32, i32, p64, p64]
+    L.zero_fsdp_init.argtypes = [i32, vp, vp, i32, i32, dbl, dbl, dbl, dbl, ctypes.POINTER(vp)]
+    L.zero_fsdp_local.argtypes = [vp, i32, p64, p64, p64]
+    L.zero_fsdp_load_master.argtypes = [vp, vp, ctypes.c_int, vp]
+    L.zero_fsdp_step.argtypes = [vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, i64, vp]
     L.zero_get_state.argtypes = [vp, vp, vp, vp, vp]
     L.zero_set_state.argtypes = [vp, vp, vp, vp, vp]
     L.zero_state_bytes.argtypes = [i32, dbl, dbl, ctypes.POINTER(dbl)]
@@ -295,3 +300,113 @@ class ShardState:
                 raise ValueError(f"{name} must be float32 with {self.shard} elements")
         _check(lib().zero_set_state(self._h, master.data_ptr(), m.data_ptr(), v.data_ptr(),
                                     _stream_handle(stream)))
+
+
+def dim0_split(dim0: int, world: int, rank: int) -> Tuple[int, int]:
+    """(first row, rows) of this rank's dim-0 shard of a parameter."""
+    f, r = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().zero_dim0_split(dim0, world, rank, ctypes.byref(f), ctypes.byref(r)))
+    return f.value, r.value
+
+
+class FsdpShardState(ShardState):
+    """One rank of the per-parameter (FSDP2-style) layout: every parameter
+    is split along dim 0 and this rank keeps fp32 master/m/v for its rows.
+    Inherits get_state / set_state / set_lr / close from ShardState."""
+
+    def __init__(self, shapes, world: int, rank: int, lr: float,
+                 betas: Tuple[float, float] = (0.9, 0.999), eps: float = 1e-8, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        self.shapes = [tuple(int(d) for d in s) for s in shapes]
+        self.world, self.rank = int(world), int(rank)
+        n = len(self.shapes)
+        dim0 = (ctypes.c_int64 * max(1, n))(*[s[0] if s else 1 for s in self.shapes])
+        rown = (ctypes.c_int64 * max(1, n))(*[
+            int(torch.Size(s[1:]).numel()) if len(s) > 1 else 1 for s in self.shapes])
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check(lib().zero_fsdp_init(n, dim0, rown, self.world, self.rank, float(lr),
+                                        float(betas[0]), float(betas[1]), float(eps),
+                                        ctypes.byref(h)))
+        self._h = h
+        s_, lo, p = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().zero_shard_info(self._h, ctypes.byref(s_), ctypes.byref(lo), ctypes.byref(p)))
+        self.shard, self.lo, self.padded = s_.value, lo.value, p.value
+        self.numel = sum(int(torch.Size(s).numel()) for s in self.shapes)
+        self.local = []
+        for k in range(n):
+            f, r, off = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+            _check(lib().zero_fsdp_local(self._h, k, ctypes.byref(f), ctypes.byref(r),
+                                         ctypes.byref(off)))
+            self.local.append((f.value, r.value, off.value))
+
+    def local_shape(self, k: int) -> Tuple[int, ...]:
+        return (self.local[k][1],) + self.shapes[k][1:]
+
+    def local_numel(self, k: int) -> int:
+        return int(torch.Size(self.local_shape(k)).numel())
+
+    def _check_full(self, ts, what):
+        if len(ts) != len(self.shapes):
+            raise ValueError(f"{what}: need {len(self.shapes)} tensors, got {len(ts)}")
+        for k, x in enumerate(ts):
+            if x is None:
+                if self.local[k][1]:
+                    raise ValueError(f"{what}[{k}] is None but this rank holds rows of it")
+                continue
+            self._dev(x, f"{what}[{k}]")
+            if tuple(x.shape) != self.shapes[k] and x.numel() != torch.Size(self.shapes[k]).numel():
+                raise ValueError(f"{what}[{k}] has shape {tuple(x.shape)}, need {self.shapes[k]}")
+
+    def load_master(self, params: Sequence[torch.Tensor], stream=None):
+        """master = this rank's rows of each full parameter; m = v = 0."""
+        self._check_full(params, "params")
+        dts = {p.dtype for p in params if p is not None}
+        if len(dts) != 1:
+            raise TypeError("params must share one dtype")
+        ptrs = _ptr_array([p.data_ptr() if p is not None else 0 for p in params])
+        _check(lib().zero_fsdp_load_master(self._h, ptrs, _dtype_code(dts.pop()),
+                                           _stream_handle(stream)))
+
+    def step(self, replica_grads: Sequence[Sequence[torch.Tensor]], t: int,
+             params_out: Sequence[torch.Tensor], stream=None):
+        """replica_grads[q][k]: replica q's full gradient of parameter k;
+        params_out[k]: this rank's local shard of parameter k (written)."""
+        if len(replica_grads) != self.world:
+            raise ValueError(f"need {self.world} replicas, got {len(replica_grads)}")
+        gdts = set()
+        for q, gl in enumerate(replica_grads):
+            self._check_full(gl, f"replica_grads[{q}]")
+            gdts |= {g.dtype for g in gl if g is not None}
+        if len(gdts) != 1:
+            raise TypeError("gradients must share one dtype")
+        if len(params_out) != len(self.shapes):
+            raise ValueError("need one output shard per parameter")
+        pdts = set()
+        for k, o in enumerate(params_out):
+            if self.local[k][1] == 0:
+                continue
+            self._dev(o, f"params_out[{k}]")
+            if o.numel() < self.local_numel(k):
+                raise ValueError(f"params_out[{k}] has {o.numel()} elements, "
+                                 f"need {self.local_numel(k)}")
+            pdts.add(o.dtype)
+        if len(pdts) > 1:
+            raise TypeError("outputs must share one dtype")
+        pdt = pdts.pop() if pdts else torch.float32
+        gptrs = _ptr_array([g.data_ptr() if g is not None else 0
+                            for gl in replica_grads for g in gl])
+        optrs = _ptr_array([o.data_ptr() if (o is not None and self.local[k][1]) else 0
+                            for k, o in enumerate(params_out)])
+        _check(lib().zero_fsdp_step(self._h, gptrs, self.world, _dtype_code(gdts.pop()), optrs,
+                                    _dtype_code(pdt), int(t), _stream_handle(stream)))
+
+    def state_pieces(self, state: Sequence[torch.Tensor]):
+        """Split (master, m, v) from get_state into per-parameter local pieces."""
+        out = []
+        for x in state:
+            out.append([x[off:off + r * (int(torch.Size(self.shapes[k][1:]).numel())
+                                          if len(self.shapes[k]) > 1 else 1)]
+                        for k, (_, r, off) in enumerate(self.local)])
+        return out

@@ -14,8 +14,17 @@
 #include "../../include/zero.h"
 #include "zero_internal.h"
 
+// One parameter of a per-parameter (dim-0) layout context.
+struct zero_fsdp_tensor {
+    int64_t dim0, row_numel;     // full shape: dim0 rows of row_numel elements
+    int64_t first_row, rows;     // this rank's rows
+    int64_t state_off;           // first element in master/m/v (multiple of 8)
+};
+
 struct zero_ctx {
     int64_t numel, shard, lo, padded;
+    bool fsdp;                               // per-parameter layout
+    std::vector<zero_fsdp_tensor> tensors;   // fsdp only
     int32_t world, rank;
     double lr, beta1, beta2, eps;
     int device;
@@ -55,6 +64,23 @@ int geometry(int64_t numel, int32_t world, int32_t rank, int64_t *shard, int64_t
     if (shard) *shard = s;
     if (lo) *lo = (int64_t)rank * s;
     if (padded) *padded = s * world;
+    return ZERO_OK;
+}
+
+void dim0_split(int64_t d0, int32_t world, int32_t rank, int64_t *first, int64_t *rows) {
+    const int64_t c = d0 / world + (d0 % world != 0 ? 1 : 0);
+    int64_t f = (int64_t)rank * c;
+    if (f > d0) f = d0;
+    int64_t e = f + c;
+    if (e > d0) e = d0;
+    *first = f;
+    *rows = e - f;
+}
+
+int reject_fsdp(const zero_ctx *c) {
+    if (c && c->fsdp)
+        return fail(ZERO_EINVAL, "this context holds the per-parameter (dim-0) layout; "
+                                 "use the zero_fsdp_* calls");
     return ZERO_OK;
 }
 
@@ -114,6 +140,7 @@ int build_flat_segments(const zero_ctx *c, const void *const *tensors, const int
                         int32_t ntensors, zero_dtype dtype, const void *flat,
                         std::vector<zk::Segment> &segs, bool to_flat) {
     if (!c) return fail(ZERO_EINVAL, "null context");
+    if (c->fsdp) return reject_fsdp(c);
     if (!tensors || !numels) return fail(ZERO_EINVAL, "null tensor or numel array");
     if (ntensors < 1) return fail(ZERO_EINVAL, "ntensors must be >= 1 (got %d)", ntensors);
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dtype);
@@ -176,48 +203,33 @@ int zero_state_bytes(int32_t stage, double numel, double world, double *bytes) {
     return ZERO_OK;
 }
 
-int zero_shard_init(int64_t numel, int32_t world, int32_t rank, double lr, double beta1,
-                    double beta2, double eps, zero_ctx **out) {
-    if (!out) return fail(ZERO_EINVAL, "null output pointer");
-    *out = nullptr;
-    int64_t shard, lo, padded;
-    int rc = geometry(numel, world, rank, &shard, &lo, &padded);
-    if (rc) return rc;
+static int check_hparams(int32_t world, double lr, double beta1, double beta2, double eps) {
     if (world > ZERO_MAX_WORLD)
         return fail(ZERO_EINVAL, "world %d exceeds ZERO_MAX_WORLD (%d)", world, ZERO_MAX_WORLD);
     if (!(beta1 > 0.0 && beta1 < 1.0) || !(beta2 > 0.0 && beta2 < 1.0))
         return fail(ZERO_EINVAL, "betas must lie in (0, 1) (got %g, %g)", beta1, beta2);
     if (!std::isfinite(lr)) return fail(ZERO_EINVAL, "lr must be finite");
     if (!std::isfinite(eps) || eps < 0.0) return fail(ZERO_EINVAL, "eps must be finite and >= 0");
+    return ZERO_OK;
+}
 
+// Device, master/m/v (`shard` elements each, zeroed) for a filled-in context.
+static int alloc_state(zero_ctx *c) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     int cus = 0;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-
-    zero_ctx *c = new (std::nothrow) zero_ctx();
-    if (!c) return fail(ZERO_ENOMEM, "host allocation failed");
-    c->numel = numel;
-    c->shard = shard;
-    c->lo = lo;
-    c->padded = padded;
-    c->world = world;
-    c->rank = rank;
-    c->lr = lr;
-    c->beta1 = beta1;
-    c->beta2 = beta2;
-    c->eps = eps;
     c->device = dev;
     c->num_cus = cus > 0 ? cus : 256;
-
-    // master | m | v, each segment rounded up to 256 bytes
-    const size_t seg = ((size_t)shard * sizeof(float) + 255) & ~(size_t)255;
+    // master | m | v, each segment rounded up to 256 bytes (at least one)
+    size_t seg = ((size_t)c->shard * sizeof(float) + 255) & ~(size_t)255;
+    if (seg == 0) seg = 256;
     e = hipMalloc(&c->state, 3 * seg);
     if (e != hipSuccess) {
         (void)hipGetLastError();
-        delete c;
+        c->state = nullptr;
         return fail(ZERO_ENOMEM, "hipMalloc of %zu bytes for master/m/v failed: %s", 3 * seg,
                     hipGetErrorString(e));
     }
@@ -228,11 +240,207 @@ int zero_shard_init(int64_t numel, int32_t world, int32_t rank, double lr, doubl
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
         (void)hipFree(c->state);
-        delete c;
+        c->state = nullptr;
         return hip_fail(e, "clearing master/m/v");
+    }
+    return ZERO_OK;
+}
+
+int zero_shard_init(int64_t numel, int32_t world, int32_t rank, double lr, double beta1,
+                    double beta2, double eps, zero_ctx **out) {
+    if (!out) return fail(ZERO_EINVAL, "null output pointer");
+    *out = nullptr;
+    int64_t shard, lo, padded;
+    int rc = geometry(numel, world, rank, &shard, &lo, &padded);
+    if (rc) return rc;
+    rc = check_hparams(world, lr, beta1, beta2, eps);
+    if (rc) return rc;
+    zero_ctx *c = new (std::nothrow) zero_ctx();
+    if (!c) return fail(ZERO_ENOMEM, "host allocation failed");
+    c->numel = numel;
+    c->shard = shard;
+    c->lo = lo;
+    c->padded = padded;
+    c->fsdp = false;
+    c->world = world;
+    c->rank = rank;
+    c->lr = lr;
+    c->beta1 = beta1;
+    c->beta2 = beta2;
+    c->eps = eps;
+    rc = alloc_state(c);
+    if (rc) {
+        delete c;
+        return rc;
     }
     *out = c;
     return ZERO_OK;
+}
+
+int zero_dim0_split(int64_t dim0, int32_t world, int32_t rank, int64_t *first_row,
+                    int64_t *rows) {
+    if (dim0 < 0) return fail(ZERO_EINVAL, "dim0 must be >= 0");
+    if (world < 1) return fail(ZERO_EINVAL, "world must be >= 1");
+    if (rank < 0 || rank >= world) return fail(ZERO_EINVAL, "rank must be in [0, world)");
+    int64_t f, r;
+    dim0_split(dim0, world, rank, &f, &r);
+    if (first_row) *first_row = f;
+    if (rows) *rows = r;
+    return ZERO_OK;
+}
+
+int zero_fsdp_init(int32_t ntensors, const int64_t *dim0, const int64_t *row_numel,
+                   int32_t world, int32_t rank, double lr, double beta1, double beta2, double eps,
+                   zero_ctx **out) {
+    if (!out) return fail(ZERO_EINVAL, "null output pointer");
+    *out = nullptr;
+    if (ntensors < 1 || !dim0 || !row_numel)
+        return fail(ZERO_EINVAL, "need ntensors >= 1 and both shape arrays");
+    if (world < 1 || rank < 0 || rank >= world)
+        return fail(ZERO_EINVAL, "rank must be in [0, world) with world >= 1");
+    if (world > ZERO_FSDP_MAX_WORLD)
+        return fail(ZERO_EUNSUPPORTED, "the per-parameter layout supports world <= %d",
+                    ZERO_FSDP_MAX_WORLD);
+    int rc = check_hparams(world, lr, beta1, beta2, eps);
+    if (rc) return rc;
+    zero_ctx *c = new (std::nothrow) zero_ctx();
+    if (!c) return fail(ZERO_ENOMEM, "host allocation failed");
+    c->fsdp = true;
+    c->world = world;
+    c->rank = rank;
+    c->lr = lr;
+    c->beta1 = beta1;
+    c->beta2 = beta2;
+    c->eps = eps;
+    int64_t off = 0, total = 0;
+    try {
+        c->tensors.resize((size_t)ntensors);
+    } catch (...) {
+        delete c;
+        return fail(ZERO_ENOMEM, "host allocation failed");
+    }
+    for (int32_t k = 0; k < ntensors; ++k) {
+        if (dim0[k] < 0 || row_numel[k] < 1) {
+            delete c;
+            return fail(ZERO_EINVAL, "tensor %d: need dim0 >= 0 and row_numel >= 1", k);
+        }
+        zero_fsdp_tensor &t = c->tensors[(size_t)k];
+        t.dim0 = dim0[k];
+        t.row_numel = row_numel[k];
+        dim0_split(t.dim0, world, rank, &t.first_row, &t.rows);
+        t.state_off = off;
+        off += (t.rows * t.row_numel + 7) / 8 * 8;   // keep every shard 32-byte aligned
+        total += t.dim0 * t.row_numel;
+    }
+    c->numel = total;
+    c->shard = off;
+    c->lo = 0;
+    c->padded = off;
+    rc = alloc_state(c);
+    if (rc) {
+        delete c;
+        return rc;
+    }
+    *out = c;
+    return ZERO_OK;
+}
+
+int zero_fsdp_local(const zero_ctx *c, int32_t k, int64_t *first_row, int64_t *rows,
+                    int64_t *state_offset) {
+    if (!c || !c->fsdp) return fail(ZERO_EINVAL, "not a per-parameter layout context");
+    if (k < 0 || k >= (int32_t)c->tensors.size()) return fail(ZERO_EINVAL, "tensor index out of range");
+    const zero_fsdp_tensor &t = c->tensors[(size_t)k];
+    if (first_row) *first_row = t.first_row;
+    if (rows) *rows = t.rows;
+    if (state_offset) *state_offset = t.state_off;
+    return ZERO_OK;
+}
+
+int zero_fsdp_load_master(zero_ctx *c, const void *const *params, zero_dtype dtype,
+                          hipStream_t stream) {
+    if (!c || !c->fsdp) return fail(ZERO_EINVAL, "not a per-parameter layout context");
+    if (!params) return fail(ZERO_EINVAL, "null parameter array");
+    if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dtype);
+    const int64_t es = (int64_t)dtype_size(dtype);
+    for (size_t k = 0; k < c->tensors.size(); ++k) {
+        const zero_fsdp_tensor &t = c->tensors[k];
+        if (t.rows == 0) continue;
+        if (!params[k]) return fail(ZERO_EINVAL, "parameter %zu is null", k);
+        if ((uintptr_t)params[k] % (uintptr_t)es) return fail(ZERO_EINVAL, "parameter %zu misaligned", k);
+        int rc = check_range(params[k], t.dim0 * t.row_numel * es, "parameter");
+        if (rc) return rc;
+    }
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    for (size_t k = 0; k < c->tensors.size(); ++k) {
+        const zero_fsdp_tensor &t = c->tensors[k];
+        if (t.rows == 0) continue;
+        const char *base = (const char *)params[k] + t.first_row * t.row_numel * es;
+        hipError_t e = zk::launch_load_master(base, dtype == ZERO_BF16, c->master + t.state_off,
+                                              c->m + t.state_off, c->v + t.state_off,
+                                              t.rows * t.row_numel, stream);
+        if (e != hipSuccess) return hip_fail(e, "load_master launch");
+    }
+    return ZERO_OK;
+}
+
+int zero_fsdp_step(zero_ctx *c, const void *const *grads, int32_t n_replicas,
+                   zero_dtype grad_dtype, void *const *params_out, zero_dtype param_dtype,
+                   int64_t t, hipStream_t stream) {
+    if (!c || !c->fsdp) return fail(ZERO_EINVAL, "not a per-parameter layout context");
+    if (n_replicas != c->world)
+        return fail(ZERO_EINVAL, "n_replicas (%d) must equal world (%d)", n_replicas, c->world);
+    if (t < 1) return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
+    if (!grads || !params_out) return fail(ZERO_EINVAL, "null gradient or output array");
+    if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
+        return fail(ZERO_EINVAL, "unknown dtype");
+    const int64_t ge = (int64_t)dtype_size(grad_dtype), pe = (int64_t)dtype_size(param_dtype);
+    const size_t nt = c->tensors.size();
+    std::vector<zk::FsdpSegment> segs;
+    try {
+        segs.reserve(nt);
+    } catch (...) {
+        return fail(ZERO_ENOMEM, "host allocation failed");
+    }
+    for (size_t k = 0; k < nt; ++k) {
+        const zero_fsdp_tensor &tt = c->tensors[k];
+        if (tt.rows == 0) continue;
+        zk::FsdpSegment sg;
+        const int64_t local = tt.rows * tt.row_numel;
+        for (int q = 0; q < n_replicas; ++q) {
+            const void *gp = grads[(size_t)q * nt + k];
+            if (!gp) return fail(ZERO_EINVAL, "gradient of replica %d, tensor %zu is null", q, k);
+            if ((uintptr_t)gp % (uintptr_t)ge)
+                return fail(ZERO_EINVAL, "gradient of replica %d, tensor %zu misaligned", q, k);
+            int rc = check_range(gp, tt.dim0 * tt.row_numel * ge, "gradient");
+            if (rc) return rc;
+            sg.grads[q] = (const char *)gp + tt.first_row * tt.row_numel * ge;
+        }
+        if (!params_out[k]) return fail(ZERO_EINVAL, "output shard %zu is null", k);
+        if ((uintptr_t)params_out[k] % (uintptr_t)pe)
+            return fail(ZERO_EINVAL, "output shard %zu misaligned", k);
+        int rc = check_range(params_out[k], local * pe, "output shard");
+        if (rc) return rc;
+        sg.out = params_out[k];
+        sg.state_off = tt.state_off;
+        sg.numel = local;
+        segs.push_back(sg);
+    }
+    if (segs.empty()) return ZERO_OK;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    zk::FsdpArgs a;
+    a.segs = segs.data();
+    a.nseg = (int)segs.size();
+    a.n = n_replicas;
+    a.grad_bf16 = grad_dtype == ZERO_BF16;
+    a.out_bf16 = param_dtype == ZERO_BF16;
+    a.master = c->master;
+    a.m = c->m;
+    a.v = c->v;
+    a.sc = make_scalars(c, t);
+    hipError_t e = zk::launch_fsdp_step(a, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "per-parameter step launch");
 }
 
 int zero_shard_info(const zero_ctx *c, int64_t *shard, int64_t *lo, int64_t *padded) {
@@ -262,6 +470,8 @@ int zero_load_master(zero_ctx *c, const void *flat, zero_dtype dtype, int64_t fl
     if (rc) return rc;
     DeviceGuard g(c->device);
     if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    rc = reject_fsdp(c);
+    if (rc) return rc;
     const char *base = (const char *)flat + (size_t)flat_offset * es;
     hipError_t e = zk::launch_load_master(base, dtype == ZERO_BF16, c->master, c->m, c->v,
                                           c->shard, stream);
@@ -298,6 +508,7 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
                        void *param_out, zero_dtype param_dtype, int64_t param_offset, int64_t t,
                        hipStream_t stream) {
     if (!c) return fail(ZERO_EINVAL, "null context");
+    if (c->fsdp) return reject_fsdp(c);
     if (begin < 0 || count < 0 || begin > c->shard - count)
         return fail(ZERO_EINVAL, "range [%lld, %lld) outside the shard of %lld elements",
                     (long long)begin, (long long)(begin + count), (long long)c->shard);
@@ -392,7 +603,7 @@ void zero_destroy(zero_ctx *c) {
     if (!c) return;
     DeviceGuard g(c->device);
     (void)hipDeviceSynchronize();
-    (void)hipFree(c->state);
+    if (c->state) (void)hipFree(c->state);
     delete c;
 }
 

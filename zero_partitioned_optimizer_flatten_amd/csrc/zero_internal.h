@@ -33,6 +33,24 @@ struct StepArgs {
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t stream);
 
+// Per-parameter (dim-0) layout: one segment per parameter's local shard.
+constexpr int kFsdpMaxWorld = 16;
+struct FsdpSegment {
+    const void *grads[kFsdpMaxWorld];   // replica q's gradient at this rank's first row
+    void *out;                          // this rank's output shard
+    int64_t state_off;                  // first element in master/m/v
+    int64_t numel;                      // local elements
+};
+struct FsdpArgs {
+    const FsdpSegment *segs;
+    int nseg;
+    int n;
+    bool grad_bf16, out_bf16;
+    float *master, *m, *v;
+    StepScalars sc;
+};
+hipError_t launch_fsdp_step(const FsdpArgs &a, hipStream_t stream);
+
 // Batched segment copy: segment s copies nbytes[s] bytes from src[s] to
 // dst[s], or writes zeros when src[s] is null. esize (2 or 4) is the
 // granularity every pointer and length is a multiple of.

@@ -257,7 +257,7 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
     float s[kVec];
     if constexpr (NR > 0 && NR <= 2 * kGroup) {
 #pragma unroll
-        for (int q0 = 0; q0 < NR; q0 += kGroup) fold_group<NR, GB>(reps, q0, NR, j, s);
+        for (int q0 = 0; q0 < NR; q0 += kGroup) fold_group<NR, GB>(reps, q0, n, j, s);
     } else {
 #pragma unroll 1
         for (int q0 = 0; q0 < n; q0 += kGroup) fold_group<NR, GB>(reps, q0, n, j, s);
@@ -388,6 +388,30 @@ step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
     }
 }
 
+// One element i of the fused step (any alignment).
+template <int NR, bool GB, bool PB>
+__device__ __forceinline__ void step_one(const Reps<NR> &reps, int n, float *__restrict__ master,
+                                         float *__restrict__ mom, float *__restrict__ var,
+                                         void *__restrict__ out, int64_t i, const StepScalars &sc) {
+    float s;
+    if (GB) s = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[0])[i]);
+    else s = reinterpret_cast<const float *>(reps.p[0])[i];
+    for (int q = 1; q < n; ++q) {
+        float x;
+        if (GB) x = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[q])[i]);
+        else x = reinterpret_cast<const float *>(reps.p[q])[i];
+        s = s + x;
+    }
+    float p = master[i], m = mom[i], v = var[i];
+    const float g = sc.n_pow2 ? s * sc.inv_n : s / sc.nf;
+    adam_update(g, p, m, v, sc);
+    master[i] = p;
+    mom[i] = m;
+    var[i] = v;
+    if (PB) reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)round_bf16(p);
+    else reinterpret_cast<float *>(out)[i] = p;
+}
+
 // Element path: any alignment, and the tail of the vector path. Lane
 // handles element i, consecutive lanes consecutive elements.
 template <bool GB, bool PB>
@@ -397,24 +421,100 @@ step_elem_kernel(Reps<0> reps, int nrep, float *__restrict__ master,
                  void *__restrict__ out, int64_t begin, int64_t end,
                  StepScalars sc) {
     const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = begin + (int64_t)blockIdx.x * kBlock + threadIdx.x; i < end; i += stride) {
-        float s;
-        if (GB) s = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[0])[i]);
-        else s = reinterpret_cast<const float *>(reps.p[0])[i];
-        for (int q = 1; q < nrep; ++q) {
-            float x;
-            if (GB) x = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[q])[i]);
-            else x = reinterpret_cast<const float *>(reps.p[q])[i];
-            s = s + x;
+    for (int64_t i = begin + (int64_t)blockIdx.x * kBlock + threadIdx.x; i < end; i += stride)
+        step_one<0, GB, PB>(reps, nrep, master, mom, var, out, i, sc);
+}
+
+// ------------------------------------------------ per-parameter (dim-0) layout
+// Each segment is one parameter's local row shard: its replica pointers
+// (already at this rank's first row), its output shard, and its place in
+// the rank's master/m/v. A workgroup takes one kBlock*8-element chunk of
+// one segment; segments whose streams are all 16-byte aligned use the
+// vector step, the rest (and every segment's last partial vector) the
+// element step.
+constexpr int kFsdpBatch = 16;       // segments per launch
+
+template <int NR>
+struct FsdpBatch {
+    Reps<NR> reps[kFsdpBatch];
+    void *out[kFsdpBatch];
+    int64_t state_off[kFsdpBatch];
+    int64_t numel[kFsdpBatch];
+    int64_t blk0[kFsdpBatch + 1];
+    int nseg;
+};
+
+template <int NR, bool EXACT, bool GB, bool PB>
+__global__ void __launch_bounds__(kBlock)
+fsdp_step_kernel(FsdpBatch<NR> b, int nrep, float *__restrict__ master,
+                 float *__restrict__ mom, float *__restrict__ var, StepScalars sc) {
+    const int64_t w = blockIdx.x;
+    int lo = 0, hi = b.nseg - 1;                 // last segment with blk0 <= w
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (b.blk0[mid] <= w) lo = mid;
+        else hi = mid - 1;
+    }
+    const int sgi = lo;
+    const int n = EXACT ? NR : nrep;
+    constexpr bool kPow2 = EXACT && (NR & (NR - 1)) == 0;
+    const bool pow2 = kPow2 || (!EXACT && sc.n_pow2);
+    const int64_t numel = b.numel[sgi];
+    float *ms = master + b.state_off[sgi];
+    float *mm = mom + b.state_off[sgi];
+    float *vs = var + b.state_off[sgi];
+    void *out = b.out[sgi];
+    const Reps<NR> &reps = b.reps[sgi];
+    bool aligned = ((uintptr_t)out % 16) == 0 && ((uintptr_t)ms % 16) == 0;
+    for (int q = 0; q < n; ++q) aligned = aligned && ((uintptr_t)reps.p[q] % 16) == 0;
+    const int64_t j = (w - b.blk0[sgi]) * kBlock + threadIdx.x;     // vector index
+    if (j * kVec >= numel) return;
+    if (aligned && (j + 1) * kVec <= numel) {
+        step_vector<NR, GB, PB>(reps, n, pow2, ms, mm, vs, out, j, sc);
+    } else {
+        const int64_t end = (j + 1) * kVec < numel ? (j + 1) * kVec : numel;
+        for (int64_t i = j * kVec; i < end; ++i) step_one<NR, GB, PB>(reps, n, ms, mm, vs, out, i, sc);
+    }
+}
+
+template <int NR, bool EXACT, bool GB, bool PB>
+hipError_t launch_fsdp_typed(const FsdpArgs &a, hipStream_t stream) {
+    const int64_t per_block = (int64_t)kBlock * kVec;
+    int i = 0;
+    while (i < a.nseg) {
+        FsdpBatch<NR> b;
+        b.nseg = 0;
+        int64_t blocks = 0;
+        while (i < a.nseg && b.nseg < kFsdpBatch) {
+            const FsdpSegment &sg = a.segs[i++];
+            if (sg.numel <= 0) continue;
+            for (int q = 0; q < a.n; ++q) b.reps[b.nseg].p[q] = sg.grads[q];
+            b.out[b.nseg] = sg.out;
+            b.state_off[b.nseg] = sg.state_off;
+            b.numel[b.nseg] = sg.numel;
+            b.blk0[b.nseg] = blocks;
+            blocks += (sg.numel + per_block - 1) / per_block;
+            b.nseg++;
         }
-        float p = master[i], m = mom[i], v = var[i];
-        const float g = sc.n_pow2 ? s * sc.inv_n : s / sc.nf;
-        adam_update(g, p, m, v, sc);
-        master[i] = p;
-        mom[i] = m;
-        var[i] = v;
-        if (PB) reinterpret_cast<uint16_t *>(out)[i] = (uint16_t)round_bf16(p);
-        else reinterpret_cast<float *>(out)[i] = p;
+        if (b.nseg == 0) continue;
+        b.blk0[b.nseg] = blocks;
+        if (blocks > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((fsdp_step_kernel<NR, EXACT, GB, PB>), dim3((unsigned)blocks),
+                           dim3(kBlock), ZK_STEP_LDS, stream, b, a.n, a.master, a.m, a.v, a.sc);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+template <bool GB, bool PB>
+hipError_t launch_fsdp_dtype(const FsdpArgs &a, hipStream_t stream) {
+    switch (a.n) {
+    case 1: return launch_fsdp_typed<1, true, GB, PB>(a, stream);
+    case 2: return launch_fsdp_typed<2, true, GB, PB>(a, stream);
+    case 4: return launch_fsdp_typed<4, true, GB, PB>(a, stream);
+    case 8: return launch_fsdp_typed<8, true, GB, PB>(a, stream);
+    default: return launch_fsdp_typed<kFsdpMaxWorld, false, GB, PB>(a, stream);
     }
 }
 
@@ -583,6 +683,16 @@ hipError_t launch_step(const StepArgs &a, hipStream_t stream) {
         return a.out_bf16 ? step_typed<true, true>(a, stream) : step_typed<true, false>(a, stream);
     }
     return a.out_bf16 ? step_typed<false, true>(a, stream) : step_typed<false, false>(a, stream);
+}
+
+hipError_t launch_fsdp_step(const FsdpArgs &a, hipStream_t stream) {
+    if (a.n < 1 || a.n > kFsdpMaxWorld) return hipErrorInvalidValue;
+    if (a.grad_bf16) {
+        return a.out_bf16 ? launch_fsdp_dtype<true, true>(a, stream)
+                          : launch_fsdp_dtype<true, false>(a, stream);
+    }
+    return a.out_bf16 ? launch_fsdp_dtype<false, true>(a, stream)
+                      : launch_fsdp_dtype<false, false>(a, stream);
 }
 
 hipError_t launch_copy_segments(const Segment *segs, int nseg, int esize, hipStream_t stream) {
