@@ -32,9 +32,10 @@ namespace zk {
 namespace {
 
 #ifndef ZK_BLOCK
-#define ZK_BLOCK 512
+#define ZK_BLOCK 64
 #endif
-constexpr int kBlock = ZK_BLOCK;     // workgroup size (wavefronts of 64 lanes)
+constexpr int kBlock = ZK_BLOCK;     // fused-step workgroup size (wavefronts of 64 lanes)
+constexpr int kElemBlock = 256;      // element path and master load
 constexpr int kVec = 8;              // elements per lane per vector step
 constexpr int kGroup = 8;            // replicas loaded together
 
@@ -64,6 +65,14 @@ constexpr int kGroup = 8;            // replicas loaded together
 #ifndef ZK_NT_OUT
 #define ZK_NT_OUT 1
 #endif
+// Non-temporal loads (only) for master/m/v.
+#ifndef ZK_NT_STATE_LD
+#define ZK_NT_STATE_LD 0
+#endif
+// Issue the replica loads before the master/m/v loads.
+#ifndef ZK_GRADS_FIRST
+#define ZK_GRADS_FIRST 0
+#endif
 // Non-temporal stores (only) for master/m/v.
 #ifndef ZK_NT_STATE_ST
 #define ZK_NT_STATE_ST 0
@@ -85,11 +94,12 @@ constexpr int kXcds = 8;
 #define ZK_COPY_VPT 1
 #endif
 // Dynamic LDS reserved (unused) per fused-step workgroup: caps how many
-// workgroups share a CU (160 KiB of LDS per CU). The default, all of it,
-// keeps one 512-lane workgroup (8 waves) per CU: measured best, since more
-// waves put more streams' requests in flight than the HBM serves well.
+// workgroups share a CU (160 KiB of LDS per CU). The default keeps seven
+// one-wave workgroups per CU: measured best (6-8 waves per CU), since more
+// waves put more of the step's 12 streams' requests in flight than the HBM
+// serves well, and fewer leave it idle.
 #ifndef ZK_STEP_LDS
-#define ZK_STEP_LDS 163840
+#define ZK_STEP_LDS 22528
 #endif
 constexpr int kStepVpt = ZK_STEP_VPT;
 
@@ -206,7 +216,8 @@ __device__ __forceinline__ void unpack(const RawVec<false> &r, float (&x)[kVec])
 
 __device__ __forceinline__ void load8(const float *base, int64_t j, float (&x)[kVec]) {
     const float4 *p = reinterpret_cast<const float4 *>(base);
-    float4 a = ld_f4<ZK_NT_STATE>(p + 2 * j), b = ld_f4<ZK_NT_STATE>(p + 2 * j + 1);
+    float4 a = ld_f4<ZK_NT_STATE || ZK_NT_STATE_LD>(p + 2 * j);
+    float4 b = ld_f4<ZK_NT_STATE || ZK_NT_STATE_LD>(p + 2 * j + 1);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
@@ -250,9 +261,11 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
                                             float *__restrict__ var, void *__restrict__ out,
                                             int64_t j, const StepScalars &sc) {
     float p[kVec], m[kVec], v[kVec];
-    load8(master, j, p);
-    load8(mom, j, m);
-    load8(var, j, v);
+    if (!ZK_GRADS_FIRST) {
+        load8(master, j, p);
+        load8(mom, j, m);
+        load8(var, j, v);
+    }
 
     float s[kVec];
     if constexpr (NR > 0 && NR <= 2 * kGroup) {
@@ -261,6 +274,11 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
     } else {
 #pragma unroll 1
         for (int q0 = 0; q0 < n; q0 += kGroup) fold_group<NR, GB>(reps, q0, n, j, s);
+    }
+    if (ZK_GRADS_FIRST) {
+        load8(master, j, p);
+        load8(mom, j, m);
+        load8(var, j, v);
     }
 
     float g[kVec];
@@ -415,13 +433,13 @@ __device__ __forceinline__ void step_one(const Reps<NR> &reps, int n, float *__r
 // Element path: any alignment, and the tail of the vector path. Lane
 // handles element i, consecutive lanes consecutive elements.
 template <bool GB, bool PB>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kElemBlock)
 step_elem_kernel(Reps<0> reps, int nrep, float *__restrict__ master,
                  float *__restrict__ mom, float *__restrict__ var,
                  void *__restrict__ out, int64_t begin, int64_t end,
                  StepScalars sc) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = begin + (int64_t)blockIdx.x * kBlock + threadIdx.x; i < end; i += stride)
+    const int64_t stride = (int64_t)gridDim.x * kElemBlock;
+    for (int64_t i = begin + (int64_t)blockIdx.x * kElemBlock + threadIdx.x; i < end; i += stride)
         step_one<0, GB, PB>(reps, nrep, master, mom, var, out, i, sc);
 }
 
@@ -556,11 +574,11 @@ template <bool GB, bool PB>
 hipError_t launch_elem(const StepArgs &a, int64_t begin, int64_t end, hipStream_t stream) {
     Reps<0> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
-    int64_t want = (end - begin + kBlock - 1) / kBlock;
+    int64_t want = (end - begin + kElemBlock - 1) / kElemBlock;
     int64_t cap = (int64_t)a.num_cus * 8;
     int grid = (int)(want < cap ? want : cap);
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((step_elem_kernel<GB, PB>), dim3(grid), dim3(kBlock), 0, stream,
+    hipLaunchKernelGGL((step_elem_kernel<GB, PB>), dim3(grid), dim3(kElemBlock), 0, stream,
                        reps, a.n, a.master, a.m, a.v, a.out, begin, end, a.sc);
     return hipGetLastError();
 }
@@ -663,11 +681,11 @@ __global__ void __launch_bounds__(kCopyBlock) copy_segments_kernel(SegBatch b) {
 // ---------------------------------------------------------- master load
 
 template <bool FB>
-__global__ void __launch_bounds__(kBlock)
+__global__ void __launch_bounds__(kElemBlock)
 load_master_kernel(const void *__restrict__ flat, float *__restrict__ master,
                    float *__restrict__ mom, float *__restrict__ var, int64_t shard) {
-    const int64_t stride = (int64_t)gridDim.x * kBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x; i < shard; i += stride) {
+    const int64_t stride = (int64_t)gridDim.x * kElemBlock;
+    for (int64_t i = (int64_t)blockIdx.x * kElemBlock + threadIdx.x; i < shard; i += stride) {
         master[i] = FB ? widen_bf16(reinterpret_cast<const uint16_t *>(flat)[i])
                        : reinterpret_cast<const float *>(flat)[i];
         mom[i] = 0.0f;
@@ -737,13 +755,13 @@ hipError_t launch_copy_segments(const Segment *segs, int nseg, int esize, hipStr
 hipError_t launch_load_master(const void *flat, bool flat_bf16, float *master, float *m,
                               float *v, int64_t shard, hipStream_t stream) {
     if (shard <= 0) return hipSuccess;
-    int64_t want = (shard + kBlock - 1) / kBlock;
+    int64_t want = (shard + kElemBlock - 1) / kElemBlock;
     int grid = (int)(want < 65536 ? want : 65536);
     if (flat_bf16)
-        hipLaunchKernelGGL(load_master_kernel<true>, dim3(grid), dim3(kBlock), 0, stream, flat,
+        hipLaunchKernelGGL(load_master_kernel<true>, dim3(grid), dim3(kElemBlock), 0, stream, flat,
                            master, m, v, shard);
     else
-        hipLaunchKernelGGL(load_master_kernel<false>, dim3(grid), dim3(kBlock), 0, stream, flat,
+        hipLaunchKernelGGL(load_master_kernel<false>, dim3(grid), dim3(kElemBlock), 0, stream, flat,
                            master, m, v, shard);
     return hipGetLastError();
 }
