@@ -73,10 +73,22 @@ def measured_traffic():
     return float(val.group(1))
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(window: int, min_seconds: float):
     """The CPU oracle as it stands, on a window of the same workload: the
     flatten of the matching 8*window gradient elements plus the shard step
-    on `window` elements with all 8 replicas, repeated for min_seconds."""
+    on `window` elements with all 8 replicas, repeated for min_seconds, on
+    all OpenMP threads and then on one thread."""
     import oracle
     rng_g = torch.Generator().manual_seed(1)
     own = (torch.randn(WORLD * window, generator=rng_g) * 1e-3).to(torch.bfloat16)
@@ -86,21 +98,31 @@ def cpu_baseline(window: int, min_seconds: float):
     orc = oracle.ShardOracle(window, 1, 0, LR, BETAS, EPS, n_replicas=WORLD)
     orc.master[:] = (torch.randn(window, generator=rng_g) * 0.02).numpy()
     out = np.zeros(window, np.uint16)
-    iters, t = 0, 1
-    t0 = time.perf_counter()
-    while True:
-        flat = oracle.flatten([own_bits], WORLD * window)
-        orc.step([flat[:window]] + peers, t, out, grad_offset=0, out_offset=0)
-        iters += 1
-        t += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds and iters >= 2:
-            break
-    return dict(value=window * iters / el, unit="shard elements/s", cores=oracle.num_threads(),
+
+    def run(seconds):
+        iters, t = 0, 1
+        t0 = time.perf_counter()
+        while True:
+            flat = oracle.flatten([own_bits], WORLD * window)
+            orc.step([flat[:window]] + peers, t, out, grad_offset=0, out_offset=0)
+            iters += 1
+            t += 1
+            el = time.perf_counter() - t0
+            if el >= seconds and iters >= 2:
+                return iters, el
+
+    threads = oracle.num_threads()
+    iters, el = run(min_seconds)
+    oracle.set_threads(1)
+    iters1, el1 = run(min_seconds / 2)
+    oracle.set_threads(threads)
+    return dict(value=window * iters / el, unit="shard elements/s", cores=threads,
                 kind="oracle",
                 sample=(f"{iters} steps of a {window}-element window of the 7e9/N=8 shard: "
                         f"flatten of {WORLD * window} bf16 gradient elements + reduce/Adam/bf16 "
-                        f"over {WORLD} replicas, {el:.1f} s wall"))
+                        f"over {WORLD} replicas, {el:.1f} s wall on {threads} OpenMP threads"),
+                single_thread_value=window * iters1 / el1,
+                cpu_model=_cpu_model(), host_cpus=os.cpu_count())
 
 
 def _time_ms(fn, reps=5):

@@ -32,6 +32,10 @@
  *     bf16 (2-byte) and fp32 (4-byte) natural alignment is required.
  *   - The library owns the context and its master/m/v buffers; the caller
  *     owns every pointer it passes, and its streams.
+ *   - Output buffers must not overlap any input of the same call (the
+ *     kernels assume no aliasing).
+ *   - A context is not locked: calls on one context must not run from
+ *     several host threads at once. Different contexts are independent.
  */
 #ifndef ZERO_SHARD_H
 #define ZERO_SHARD_H
@@ -111,6 +115,18 @@ int zero_load_master(zero_ctx *ctx, const void *flat_params, zero_dtype dtype,
 int zero_flatten(const zero_ctx *ctx, const void *const *srcs,
                  const int64_t *numels, int32_t ntensors, zero_dtype dtype,
                  void *dst, hipStream_t stream);
+
+/* zero_flatten restricted to flat elements [flat_begin, flat_begin +
+ * flat_count) of the padded vector (pad included): a window of the flatten,
+ * e.g. one gradient bucket, or this rank's slice ahead of the rest. Windows
+ * that tile [0, padded) give exactly zero_flatten's result; disjoint
+ * windows may run on different streams. Same argument rules as
+ * zero_flatten, plus 0 <= flat_begin, 0 <= flat_count, flat_begin +
+ * flat_count <= padded (EINVAL otherwise). */
+int zero_flatten_range(const zero_ctx *ctx, const void *const *srcs,
+                       const int64_t *numels, int32_t ntensors, zero_dtype dtype,
+                       void *dst, int64_t flat_begin, int64_t flat_count,
+                       hipStream_t stream);
 
 /* The inverse ([ZeRO and FSDP], ZeroAdam.step, the copy of the gathered
  * vector back into each parameter): dsts[t] receives flat elements

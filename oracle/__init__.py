@@ -70,6 +70,7 @@ def load(path: str):
                                     vp, i32, i64]
     L.oracle_load_master.argtypes = [vp, i32, i64, i64, vp, vp, vp]
     L.oracle_num_threads.restype = ctypes.c_int
+    L.oracle_set_threads.argtypes = [ctypes.c_int]
     return L
 
 
@@ -133,6 +134,10 @@ def state_bytes(shard: int) -> int:
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
 
 
 # ------------------------------------------------------------------ flatten

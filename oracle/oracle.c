@@ -307,6 +307,16 @@ int oracle_load_master(const void *flat, int32_t is_bf16, int64_t lo,
     return ORACLE_OK;
 }
 
+/* Set the number of threads the parallel loops use (timing only). */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Threads the parallel loops above use (for reporting). */
 int oracle_num_threads(void)
 {

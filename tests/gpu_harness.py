@@ -67,10 +67,19 @@ def bf16_ulp(got: np.ndarray, ref: np.ndarray) -> int:
     return int(d.max()) if d.size else 0
 
 
+def _isnan_bits(a: np.ndarray) -> np.ndarray:
+    if a.dtype == np.uint16:
+        return ((a & 0x7F80) == 0x7F80) & ((a & 0x007F) != 0)
+    return np.isnan(a)
+
+
 def mismatches(got: np.ndarray, ref: np.ndarray) -> int:
+    """Elements whose bit patterns differ; a NaN against a NaN counts as
+    equal (NaN payload and sign are not part of the parity bar)."""
     gv = got.view(np.uint32 if got.dtype == np.float32 else np.uint16)
     rv = ref.view(np.uint32 if ref.dtype == np.float32 else np.uint16)
-    return int(np.count_nonzero(gv != rv))
+    both_nan = _isnan_bits(got) & _isnan_bits(ref)
+    return int(np.count_nonzero((gv != rv) & ~both_nan))
 
 
 def assert_state_parity(label, gpu_state, ref_state, out_got=None, out_ref=None):

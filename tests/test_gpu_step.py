@@ -342,3 +342,76 @@ def test_library_range_check_on_exact_allocations():
     finally:
         hip.hipFree(g)
         hip.hipFree(o)
+
+
+@pytest.mark.parametrize("lr,betas,eps,t0", [
+    (3e-4, (0.85, 0.98), 1e-6, 1),
+    (1e-2, (0.5, 0.75), 0.0, 1),
+    (1e-3, (0.9, 0.999), 1e-8, 997),       # far into training: 1-b^t near 1
+    (5e-5, (0.95, 0.9999), 1e-12, 20000),
+])
+def test_hyperparameters_and_late_steps(lr, betas, eps, t0):
+    """Other Adam hyperparameters and step numbers far from 1 (bias
+    correction near 1; the page's counter passed explicitly)."""
+    numel, world, rank = 100_003, 4, 2
+    dev = torch.device("cuda")
+    st = zero.ShardState(numel, world, rank, lr, betas, eps)
+    orc = oracle.ShardOracle(numel, world, rank, lr, betas, eps)
+    P = st.padded
+    p = torch.zeros(P, device=dev)
+    p[:numel] = synth.params(numel, device=dev)
+    st.load_master(p)
+    orc.load_master(bits(p))
+    out = torch.zeros(P, dtype=torch.bfloat16, device=dev)
+    out_h = np.zeros(P, np.uint16)
+    for t in range(t0, t0 + 4):
+        reps = []
+        for q in range(world):
+            f = torch.zeros(P, dtype=torch.bfloat16, device=dev)
+            f[:numel] = synth.gaussian(numel, 1e-3, synth.grad_seed(t % 1000, q), torch.bfloat16, dev)
+            reps.append(f)
+        st.step(reps, t, out)
+        orc.step([bits(r) for r in reps], t, out_h)
+    torch.cuda.synchronize()
+    assert_bitexact_state(f"hparams {lr} {betas} {eps} t0={t0}", gpu_state(st),
+                          [orc.master, orc.m, orc.v], bits(out), out_h)
+    st.close()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_flatten_windows(dtype):
+    """Windows tiling [0, padded) on 3 streams give zero_flatten's bytes;
+    a single window writes nothing outside itself."""
+    dev = torch.device("cuda")
+    shapes = synth.ragged_shapes(7, 29, 50_000) + [(1,)]
+    numel = synth.numel_of(shapes)
+    st = zero.ShardState(numel, 8, 0, 1e-3)
+    P = st.padded
+    srcs = [synth.gaussian(int(np.prod(s)), 1.0, k, dtype, dev) for k, s in enumerate(shapes)]
+    fill = -1 if dtype == torch.bfloat16 else -7
+    idt = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    whole = torch.full((P,), fill, dtype=idt, device=dev).view(dtype)
+    st.flatten(srcs, whole)
+    tiled = torch.full((P,), fill, dtype=idt, device=dev).view(dtype)
+    g = torch.Generator().manual_seed(3)
+    cuts = sorted(set(int(x) for x in torch.randint(1, P, (12,), generator=g)))
+    bounds = [0] + cuts + [P]
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    cur = torch.cuda.current_stream()
+    for i in range(len(bounds) - 1):
+        s = streams[i % 3]
+        s.wait_stream(cur)
+        st.flatten(srcs, tiled, stream=s, window=(bounds[i], bounds[i + 1] - bounds[i]))
+    for s in streams:
+        cur.wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(whole.view(idt), tiled.view(idt))
+    one = torch.full((P,), fill, dtype=idt, device=dev).view(dtype)
+    b, n = P // 3 + 1, P // 5
+    st.flatten(srcs, one, window=(b, n))
+    torch.cuda.synchronize()
+    assert torch.equal(one[b:b + n].view(idt), whole[b:b + n].view(idt))
+    assert bool((one[:b].view(idt) == fill).all()) and bool((one[b + n:].view(idt) == fill).all())
+    with pytest.raises(zero.ZeroError):
+        st.flatten(srcs, one, window=(P - 2, 3))
+    st.close()

@@ -59,6 +59,7 @@ def lib():
     L.zero_load_master.argtypes = [vp, vp, ctypes.c_int, i64, vp]
     L.zero_flatten.argtypes = [vp, vp, vp, i32, ctypes.c_int, vp, vp]
     L.zero_unflatten.argtypes = [vp, vp, i32, vp, ctypes.c_int, vp, vp]
+    L.zero_flatten_range.argtypes = [vp, vp, vp, i32, ctypes.c_int, vp, i64, i64, vp]
     L.zero_step.argtypes = [vp, vp, i32, ctypes.c_int, i64, vp, ctypes.c_int, i64, i64, vp]
     L.zero_step_range.argtypes = [vp, i64, i64, vp, i32, ctypes.c_int, i64, vp, ctypes.c_int,
                                   i64, i64, vp]
@@ -185,8 +186,10 @@ class ShardState:
                                       _dtype_code(flat_params.dtype), off,
                                       _stream_handle(stream)))
 
-    def flatten(self, tensors: Sequence[torch.Tensor], out: torch.Tensor, stream=None):
-        """out[:numel] = concatenation of the tensors; out[numel:padded] = 0."""
+    def flatten(self, tensors: Sequence[torch.Tensor], out: torch.Tensor, stream=None,
+                window: Optional[Tuple[int, int]] = None):
+        """out[:numel] = concatenation of the tensors; out[numel:padded] = 0.
+        window=(begin, count) writes only flat elements [begin, begin+count)."""
         dt = out.dtype
         self._dev(out, "out")
         if out.numel() < self.padded:
@@ -197,8 +200,14 @@ class ShardState:
                 raise TypeError(f"tensors[{i}] is {t.dtype}, out is {dt}")
         numels = (ctypes.c_int64 * max(1, len(tensors)))(*[t.numel() for t in tensors])
         ptrs = _ptr_array([t.data_ptr() for t in tensors])
-        _check(lib().zero_flatten(self._h, ptrs, numels, len(tensors), _dtype_code(dt),
-                                  out.data_ptr(), _stream_handle(stream)))
+        if window is None:
+            _check(lib().zero_flatten(self._h, ptrs, numels, len(tensors), _dtype_code(dt),
+                                      out.data_ptr(), _stream_handle(stream)))
+        else:
+            b, n = window
+            _check(lib().zero_flatten_range(self._h, ptrs, numels, len(tensors), _dtype_code(dt),
+                                            out.data_ptr(), int(b), int(n),
+                                            _stream_handle(stream)))
 
     def unflatten(self, flat: torch.Tensor, tensors: Sequence[torch.Tensor], stream=None):
         """Copy flat[off_t : off_t + numel_t] into each tensor, in order."""

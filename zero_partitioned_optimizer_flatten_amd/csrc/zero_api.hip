@@ -490,6 +490,39 @@ int zero_flatten(const zero_ctx *c, const void *const *srcs, const int64_t *nume
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "flatten launch");
 }
 
+int zero_flatten_range(const zero_ctx *c, const void *const *srcs, const int64_t *numels,
+                       int32_t ntensors, zero_dtype dtype, void *dst, int64_t flat_begin,
+                       int64_t flat_count, hipStream_t stream) {
+    std::vector<zk::Segment> segs;
+    int rc = build_flat_segments(c, srcs, numels, ntensors, dtype, dst, segs, true);
+    if (rc) return rc;
+    if (flat_begin < 0 || flat_count < 0 || flat_begin > c->padded - flat_count)
+        return fail(ZERO_EINVAL, "window [%lld, %lld) outside the padded length %lld",
+                    (long long)flat_begin, (long long)(flat_begin + flat_count),
+                    (long long)c->padded);
+    // clip every segment to the window (segments are laid out in flat order)
+    const int64_t es = (int64_t)dtype_size(dtype);
+    const char *base = (const char *)dst;
+    const int64_t wb = flat_begin * es, we = (flat_begin + flat_count) * es;
+    std::vector<zk::Segment> clipped;
+    clipped.reserve(segs.size());
+    for (const zk::Segment &sg : segs) {
+        const int64_t b = (const char *)sg.dst - base, e = b + sg.nbytes;
+        const int64_t cb = b > wb ? b : wb, ce = e < we ? e : we;
+        if (cb >= ce) continue;
+        zk::Segment x;
+        x.src = sg.src ? (const char *)sg.src + (cb - b) : nullptr;
+        x.dst = (char *)sg.dst + (cb - b);
+        x.nbytes = ce - cb;
+        clipped.push_back(x);
+    }
+    if (clipped.empty()) return ZERO_OK;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    hipError_t e = zk::launch_copy_segments(clipped.data(), (int)clipped.size(), (int)es, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "flatten launch");
+}
+
 int zero_unflatten(const zero_ctx *c, const void *flat, int32_t ntensors, const int64_t *numels,
                    zero_dtype dtype, void *const *dsts, hipStream_t stream) {
     std::vector<zk::Segment> segs;
