@@ -258,8 +258,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one rank's shard step on one GPU; runs on more than one "
-              "GPU are not supported by this build (the other ranks are simulated as "
-              "gradient replicas on the same device).", file=sys.stderr)
+              "GPU are not supported (the other ranks are simulated as gradient replicas "
+              "on the same device).", file=sys.stderr)
         sys.exit(2)
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -357,7 +357,7 @@ def main():
         "config": {"workload": "flat7b_n8_rank0: 7e9-element flat vector, N=8 simulated "
                                "ranks, rank 0 shard of 875,000,000",
                    "numel": NUMEL, "world": WORLD, "rank": RANK, "shard": S,
-                   "global_batch": None, "seq_len": None, "parallelism": "zero2-shard, 1 GPU"},
+                   "parallelism": "zero2-shard, 1 GPU"},
         "step_hbm_gbps": (k1_bytes + k2_bytes) / (ms_per_step * 1e-3) / 1e9,
         "kernels": {
             "fused_step": {"ms_mean": float(step_ms.mean()), "ms_min": float(step_ms.min()),

@@ -59,7 +59,7 @@ enum {
     ZERO_EINVAL = -1,        /* an argument is out of range or null */
     ZERO_ENOMEM = -2,        /* device or host allocation failed */
     ZERO_EHIP = -3,          /* a HIP runtime call failed */
-    ZERO_EUNSUPPORTED = -4   /* valid request this build cannot serve */
+    ZERO_EUNSUPPORTED = -4   /* valid request the library cannot serve */
 };
 
 /* Largest world (number of gradient replicas) a step accepts. */
