@@ -214,7 +214,11 @@ static int check_hparams(int32_t world, double lr, double beta1, double beta2, d
 }
 
 // Device, master/m/v (`shard` elements each, zeroed) for a filled-in context.
-static int alloc_state(zero_ctx *c) {
+// Each array starts `shift` elements past a 256-byte boundary: with shift =
+// lo mod 4, element i of the state and element lo + i of any 16-byte
+// aligned full flat buffer share their offset within 16 bytes, so a step
+// on full flat buffers at an unaligned lo still runs 16-byte vectors.
+static int alloc_state(zero_ctx *c, int shift) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -224,7 +228,7 @@ static int alloc_state(zero_ctx *c) {
     c->device = dev;
     c->num_cus = cus > 0 ? cus : 256;
     // master | m | v, each segment rounded up to 256 bytes (at least one)
-    size_t seg = ((size_t)c->shard * sizeof(float) + 255) & ~(size_t)255;
+    size_t seg = (((size_t)c->shard + (size_t)shift) * sizeof(float) + 255) & ~(size_t)255;
     if (seg == 0) seg = 256;
     e = hipMalloc(&c->state, 3 * seg);
     if (e != hipSuccess) {
@@ -233,9 +237,9 @@ static int alloc_state(zero_ctx *c) {
         return fail(ZERO_ENOMEM, "hipMalloc of %zu bytes for master/m/v failed: %s", 3 * seg,
                     hipGetErrorString(e));
     }
-    c->master = (float *)c->state;
-    c->m = (float *)((char *)c->state + seg);
-    c->v = (float *)((char *)c->state + 2 * seg);
+    c->master = (float *)c->state + shift;
+    c->m = (float *)((char *)c->state + seg) + shift;
+    c->v = (float *)((char *)c->state + 2 * seg) + shift;
     e = hipMemset(c->state, 0, 3 * seg);
     if (e == hipSuccess) e = hipDeviceSynchronize();
     if (e != hipSuccess) {
@@ -268,7 +272,7 @@ int zero_shard_init(int64_t numel, int32_t world, int32_t rank, double lr, doubl
     c->beta1 = beta1;
     c->beta2 = beta2;
     c->eps = eps;
-    rc = alloc_state(c);
+    rc = alloc_state(c, (int)(lo % 4));
     if (rc) {
         delete c;
         return rc;
@@ -336,7 +340,7 @@ int zero_fsdp_init(int32_t ntensors, const int64_t *dim0, const int64_t *row_num
     c->shard = off;
     c->lo = 0;
     c->padded = off;
-    rc = alloc_state(c);
+    rc = alloc_state(c, 0);
     if (rc) {
         delete c;
         return rc;

@@ -583,17 +583,44 @@ hipError_t launch_elem(const StepArgs &a, int64_t begin, int64_t end, hipStream_
     return hipGetLastError();
 }
 
+// Smallest h in [0, 8) at which every stream sits on a 16-byte boundary
+// (element h of a bf16 stream at byte 2h, of an fp32 stream at 4h), or -1.
+inline int common_head(const StepArgs &a) {
+    const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
+    for (int h = 0; h < kVec; ++h) {
+        bool ok = ((uintptr_t)a.master + 4u * h) % 16 == 0 && ((uintptr_t)a.m + 4u * h) % 16 == 0 &&
+                  ((uintptr_t)a.v + 4u * h) % 16 == 0 && ((uintptr_t)a.out + (uintptr_t)oe * h) % 16 == 0;
+        for (int q = 0; q < a.n && ok; ++q) ok = ((uintptr_t)a.grads[q] + (uintptr_t)ge * h) % 16 == 0;
+        if (ok) return h;
+    }
+    return -1;
+}
+
 template <bool GB, bool PB>
 hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
-    bool aligned = ((uintptr_t)a.out % 16) == 0 && ((uintptr_t)a.master % 16) == 0 &&
-                   ((uintptr_t)a.m % 16) == 0 && ((uintptr_t)a.v % 16) == 0;
-    for (int q = 0; q < a.n && aligned; ++q) aligned = ((uintptr_t)a.grads[q] % 16) == 0;
-    int64_t nvec = aligned ? a.shard / kVec : 0;
-    if (nvec > 0) {
-        hipError_t e = dispatch_vec<GB, PB>(a, nvec, stream);
+    // Vector path from the first element at which all streams are 16-byte
+    // aligned; the few elements before it and the ragged tail take the
+    // element path (same arithmetic).
+    const int h = common_head(a);
+    if (h < 0 || a.shard - h < kVec) return launch_elem<GB, PB>(a, 0, a.shard, stream);
+    const int64_t nvec = (a.shard - h) / kVec;
+    if (h > 0) {
+        hipError_t e = launch_elem<GB, PB>(a, 0, h, stream);
         if (e != hipSuccess) return e;
     }
-    if (nvec * kVec < a.shard) return launch_elem<GB, PB>(a, nvec * kVec, a.shard, stream);
+    StepArgs b = a;
+    const void *shifted[ZERO_MAX_WORLD];
+    const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
+    for (int q = 0; q < a.n; ++q) shifted[q] = (const char *)a.grads[q] + (int64_t)ge * h;
+    b.grads = shifted;
+    b.master = a.master + h;
+    b.m = a.m + h;
+    b.v = a.v + h;
+    b.out = (char *)a.out + (int64_t)oe * h;
+    hipError_t e = dispatch_vec<GB, PB>(b, nvec, stream);
+    if (e != hipSuccess) return e;
+    const int64_t done = h + nvec * kVec;
+    if (done < a.shard) return launch_elem<GB, PB>(a, done, a.shard, stream);
     return hipSuccess;
 }
 
