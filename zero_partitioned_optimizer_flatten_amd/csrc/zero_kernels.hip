@@ -39,60 +39,10 @@ constexpr int kElemBlock = 256;      // element path and master load
 constexpr int kVec = 8;              // elements per lane per vector step
 constexpr int kGroup = 8;            // replicas loaded together
 
-// Launch shape of the fused step: each workgroup owns kStepVpt * kBlock
-// consecutive 8-element vectors (one pass, no grid-stride loop), so the
-// waves in flight at any moment cover one contiguous, sliding window of
-// every stream. ZK_STEP_VPT=0 selects a persistent grid-stride launch;
-// ZK_STEP_VPT=-1 a persistent launch of ZK_STEP_BPC workgroups per CU in
-// which each workgroup walks its own contiguous range.
-#ifndef ZK_STEP_VPT
-#define ZK_STEP_VPT 1
-#endif
-#ifndef ZK_STEP_BPC
-#define ZK_STEP_BPC 8
-#endif
-// With ZK_STEP_VPT=2: issue both vectors' loads before computing either.
-#ifndef ZK_STEP_PAIR
-#define ZK_STEP_PAIR 0
-#endif
-// Non-temporal (streaming) hints: every stream is touched once per step.
-#ifndef ZK_NT_GRAD
-#define ZK_NT_GRAD 1
-#endif
-#ifndef ZK_NT_STATE
-#define ZK_NT_STATE 0
-#endif
-#ifndef ZK_NT_OUT
-#define ZK_NT_OUT 1
-#endif
-// Non-temporal loads (only) for master/m/v.
-#ifndef ZK_NT_STATE_LD
-#define ZK_NT_STATE_LD 0
-#endif
-// Issue the replica loads before the master/m/v loads.
-#ifndef ZK_GRADS_FIRST
-#define ZK_GRADS_FIRST 0
-#endif
-// Non-temporal stores (only) for master/m/v.
-#ifndef ZK_NT_STATE_ST
-#define ZK_NT_STATE_ST 0
-#endif
-// XCD-aware workgroup order: the dispatcher deals workgroups to the 8 XCDs
-// round-robin; remapping makes XCD x walk its own contiguous eighth.
-#ifndef ZK_XCD_REMAP
-#define ZK_XCD_REMAP 0
-#endif
-constexpr int kXcds = 8;
-#ifndef ZK_NT_COPY
-#define ZK_NT_COPY 1
-#endif
-// Segment copy: workgroup size, and 16-byte vectors per lane per chunk.
-#ifndef ZK_COPY_BLOCK
-#define ZK_COPY_BLOCK 64
-#endif
-#ifndef ZK_COPY_VPT
-#define ZK_COPY_VPT 1
-#endif
+// Launch shape of the fused step: one 8-element vector per lane and one pass
+// over the shard (no grid-stride loop), so the waves in flight at any moment
+// cover one contiguous, sliding window of every stream.
+//
 // Dynamic LDS reserved (unused) per fused-step workgroup: caps how many
 // workgroups share a CU (160 KiB of LDS per CU). The default keeps seven
 // one-wave workgroups per CU: measured best (6-8 waves per CU), since more
@@ -101,7 +51,22 @@ constexpr int kXcds = 8;
 #ifndef ZK_STEP_LDS
 #define ZK_STEP_LDS 22528
 #endif
-constexpr int kStepVpt = ZK_STEP_VPT;
+// Non-temporal (streaming) hints. The replicas are read once and the
+// parameter output written once; hints on the read-modify-write master/m/v
+// streams measured slower, so those use the default policy.
+#ifndef ZK_NT_GRAD
+#define ZK_NT_GRAD 1
+#endif
+#ifndef ZK_NT_OUT
+#define ZK_NT_OUT 1
+#endif
+#ifndef ZK_NT_COPY
+#define ZK_NT_COPY 1
+#endif
+// Segment copy: workgroup size (one 16-byte vector per lane per chunk).
+#ifndef ZK_COPY_BLOCK
+#define ZK_COPY_BLOCK 64
+#endif
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -216,8 +181,7 @@ __device__ __forceinline__ void unpack(const RawVec<false> &r, float (&x)[kVec])
 
 __device__ __forceinline__ void load8(const float *base, int64_t j, float (&x)[kVec]) {
     const float4 *p = reinterpret_cast<const float4 *>(base);
-    float4 a = ld_f4<ZK_NT_STATE || ZK_NT_STATE_LD>(p + 2 * j);
-    float4 b = ld_f4<ZK_NT_STATE || ZK_NT_STATE_LD>(p + 2 * j + 1);
+    float4 a = ld_f4<false>(p + 2 * j), b = ld_f4<false>(p + 2 * j + 1);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
@@ -261,11 +225,9 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
                                             float *__restrict__ var, void *__restrict__ out,
                                             int64_t j, const StepScalars &sc) {
     float p[kVec], m[kVec], v[kVec];
-    if (!ZK_GRADS_FIRST) {
-        load8(master, j, p);
-        load8(mom, j, m);
-        load8(var, j, v);
-    }
+    load8(master, j, p);
+    load8(mom, j, m);
+    load8(var, j, v);
 
     float s[kVec];
     if constexpr (NR > 0 && NR <= 2 * kGroup) {
@@ -274,11 +236,6 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
     } else {
 #pragma unroll 1
         for (int q0 = 0; q0 < n; q0 += kGroup) fold_group<NR, GB>(reps, q0, n, j, s);
-    }
-    if (ZK_GRADS_FIRST) {
-        load8(master, j, p);
-        load8(mom, j, m);
-        load8(var, j, v);
     }
 
     float g[kVec];
@@ -292,9 +249,9 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
 #pragma unroll
     for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
 
-    store8<ZK_NT_STATE || ZK_NT_STATE_ST>(master, j, p);
-    store8<ZK_NT_STATE || ZK_NT_STATE_ST>(mom, j, m);
-    store8<ZK_NT_STATE || ZK_NT_STATE_ST>(var, j, v);
+    store8<false>(master, j, p);
+    store8<false>(mom, j, m);
+    store8<false>(var, j, v);
     if (PB) {
         uint4 o;
         o.x = round_bf16(p[0]) | (round_bf16(p[1]) << 16);
@@ -304,58 +261,6 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
         st_u4<ZK_NT_OUT>(reinterpret_cast<uint4 *>(out) + j, o);
     } else {
         store8<ZK_NT_OUT>(reinterpret_cast<float *>(out), j, p);
-    }
-}
-
-// Two vectors per lane with both vectors' loads issued before either is
-// computed (more bytes in flight per wave).
-template <int NR, bool GB, bool PB>
-__device__ __forceinline__ void step_vector_pair(const Reps<NR> &reps, bool pow2,
-                                                 float *__restrict__ master,
-                                                 float *__restrict__ mom,
-                                                 float *__restrict__ var,
-                                                 void *__restrict__ out, int64_t j0, int64_t j1,
-                                                 const StepScalars &sc) {
-    static_assert(NR > 0 && NR <= kGroup, "pair path: compile-time N <= 8");
-    float p[2][kVec], m[2][kVec], v[2][kVec];
-    RawVec<GB> raw[2][NR];
-    const int64_t js[2] = {j0, j1};
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        load8(master, js[h], p[h]);
-        load8(mom, js[h], m[h]);
-        load8(var, js[h], v[h]);
-#pragma unroll
-        for (int k = 0; k < NR; ++k) raw[h][k] = load_vec<GB>(reps.p[k], js[h]);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float s[kVec];
-#pragma unroll
-        for (int k = 0; k < NR; ++k) {
-            float x[kVec];
-            unpack(raw[h][k], x);
-#pragma unroll
-            for (int e = 0; e < kVec; ++e) s[e] = k == 0 ? x[e] : s[e] + x[e];
-        }
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-            const float g = pow2 ? s[e] * sc.inv_n : s[e] / sc.nf;
-            adam_update(g, p[h][e], m[h][e], v[h][e], sc);
-        }
-        store8<ZK_NT_STATE || ZK_NT_STATE_ST>(master, js[h], p[h]);
-        store8<ZK_NT_STATE || ZK_NT_STATE_ST>(mom, js[h], m[h]);
-        store8<ZK_NT_STATE || ZK_NT_STATE_ST>(var, js[h], v[h]);
-        if (PB) {
-            uint4 o;
-            o.x = round_bf16(p[h][0]) | (round_bf16(p[h][1]) << 16);
-            o.y = round_bf16(p[h][2]) | (round_bf16(p[h][3]) << 16);
-            o.z = round_bf16(p[h][4]) | (round_bf16(p[h][5]) << 16);
-            o.w = round_bf16(p[h][6]) | (round_bf16(p[h][7]) << 16);
-            st_u4<ZK_NT_OUT>(reinterpret_cast<uint4 *>(out) + js[h], o);
-        } else {
-            store8<ZK_NT_OUT>(reinterpret_cast<float *>(out), js[h], p[h]);
-        }
     }
 }
 
@@ -371,39 +276,8 @@ step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
     const int n = NR > 0 ? NR : nrep;
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
-    if constexpr (kStepVpt == 2 && ZK_STEP_PAIR && NR > 0 && NR <= kGroup) {
-        const int64_t j0 = (int64_t)blockIdx.x * (kBlock * 2) + threadIdx.x;
-        const int64_t j1 = j0 + kBlock;
-        if (j1 < nvec) {
-            step_vector_pair<NR, GB, PB>(reps, pow2, master, mom, var, out, j0, j1, sc);
-        } else if (j0 < nvec) {
-            step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j0, sc);
-        }
-    } else if constexpr (kStepVpt > 0) {
-        int64_t bid = blockIdx.x;
-        if (ZK_XCD_REMAP) {      // grid is a multiple of kXcds
-            const int64_t per = gridDim.x / kXcds;
-            bid = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
-        }
-        const int64_t base = bid * (kBlock * kStepVpt) + threadIdx.x;
-#pragma unroll
-        for (int k = 0; k < kStepVpt; ++k) {
-            const int64_t j = base + (int64_t)k * kBlock;
-            if (j < nvec) step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
-        }
-    } else if constexpr (kStepVpt < 0) {
-        const int64_t G = gridDim.x;
-        int64_t per = (nvec + G - 1) / G;
-        per = (per + kBlock - 1) / kBlock * kBlock;
-        const int64_t beg = (int64_t)blockIdx.x * per;
-        const int64_t end = beg + per < nvec ? beg + per : nvec;
-        for (int64_t j = beg + threadIdx.x; j < end; j += kBlock)
-            step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
-    } else {
-        const int64_t stride = (int64_t)gridDim.x * kBlock;
-        for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < nvec; j += stride)
-            step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
-    }
+    const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (j < nvec) step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
 }
 
 // One element i of the fused step (any alignment).
@@ -540,18 +414,9 @@ template <int NR, bool GB, bool PB>
 hipError_t launch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
     Reps<NR> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
-    int64_t grid;
-    if (kStepVpt > 0) {
-        const int64_t per_block = (int64_t)kBlock * kStepVpt;
-        grid = (nvec + per_block - 1) / per_block;
-        if (ZK_XCD_REMAP) grid = (grid + kXcds - 1) / kXcds * kXcds;
-        // a dispatch holds at most 2^32-1 work-items
-        if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
-    } else {
-        const int64_t want = (nvec + kBlock - 1) / kBlock;
-        const int64_t cap = (int64_t)a.num_cus * (kStepVpt < 0 ? ZK_STEP_BPC : 8);
-        grid = want < cap ? want : cap;
-    }
+    const int64_t grid = (nvec + kBlock - 1) / kBlock;
+    // a dispatch holds at most 2^32-1 work-items
+    if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB>), dim3((unsigned)grid), dim3(kBlock),
                        ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, a.sc);
     return hipGetLastError();
@@ -628,7 +493,7 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
 
 constexpr int kSegBatch = 64;                 // segments per launch
 constexpr int kCopyBlock = ZK_COPY_BLOCK;
-constexpr int64_t kChunk = (int64_t)kCopyBlock * 16 * ZK_COPY_VPT;   // bytes per workgroup
+constexpr int64_t kChunk = (int64_t)kCopyBlock * 16;   // bytes per workgroup
 
 struct SegBatch {
     const char *src[kSegBatch];
@@ -685,22 +550,9 @@ __global__ void __launch_bounds__(kCopyBlock) copy_segments_kernel(SegBatch b) {
     const int64_t nv = (len - head) / 16;
     const uint4 *s4 = src ? reinterpret_cast<const uint4 *>(src + head) : nullptr;
     uint4 *d4 = reinterpret_cast<uint4 *>(dst + head);
-    int64_t k = threadIdx.x;
-    if (s4) {
-        for (; k + 3 * kCopyBlock < nv; k += 4 * kCopyBlock) {
-            uint4 x0 = ld_u4<ZK_NT_COPY>(s4 + k), x1 = ld_u4<ZK_NT_COPY>(s4 + k + kCopyBlock);
-            uint4 x2 = ld_u4<ZK_NT_COPY>(s4 + k + 2 * kCopyBlock);
-            uint4 x3 = ld_u4<ZK_NT_COPY>(s4 + k + 3 * kCopyBlock);
-            st_u4<ZK_NT_COPY>(d4 + k, x0);
-            st_u4<ZK_NT_COPY>(d4 + k + kCopyBlock, x1);
-            st_u4<ZK_NT_COPY>(d4 + k + 2 * kCopyBlock, x2);
-            st_u4<ZK_NT_COPY>(d4 + k + 3 * kCopyBlock, x3);
-        }
-        for (; k < nv; k += kCopyBlock) st_u4<ZK_NT_COPY>(d4 + k, ld_u4<ZK_NT_COPY>(s4 + k));
-    } else {
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-        for (; k < nv; k += kCopyBlock) st_u4<ZK_NT_COPY>(d4 + k, z);
-    }
+    // a chunk is one 16-byte vector per lane
+    for (int64_t k = threadIdx.x; k < nv; k += kCopyBlock)
+        st_u4<ZK_NT_COPY>(d4 + k, s4 ? ld_u4<ZK_NT_COPY>(s4 + k) : make_uint4(0u, 0u, 0u, 0u));
     const int64_t done = head + nv * 16;
     copy_elems_any(src ? src + done : nullptr, dst + done, len - done, b.esize);
 }
