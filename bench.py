@@ -15,6 +15,10 @@ Prints one JSON line. `value` is shard elements updated per second over the
 whole step; `roofline` describes the fused step kernel (HIP events on the
 launch stream); `cpu_baseline` times the CPU oracle on a bounded window of
 the same workload on this host.
+
+`--workload` times one of the other shards instead (the 1,000,003-element,
+GPT-2-small, Llama-13B and 70e9/N=64 cases, built as in the parity tests);
+those lines carry no CPU baseline and no extras.
 """
 from __future__ import annotations
 
@@ -243,11 +247,103 @@ def copy_ceiling(nbytes: int, reps: int = 5):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+WORKLOADS = {
+    "flat7b_n8_rank0": dict(
+        desc="7e9-element flat vector, N=8 simulated ranks, rank 0 shard of 875,000,000",
+        numel=7_000_000_000, world=8, rank=0, shapes=None, gdt=torch.bfloat16, std=1e-3,
+        outliers=False, peers="slice", out="full", flatten=True),
+    "flat1m_n4_rank3": dict(
+        desc="1,000,003-element flat vector (one tensor), N=4, rank 3 (one pad element), fp32 "
+             "gradients N(0,0.01), full flat replicas; cache-resident (10.5 MB per step)",
+        numel=1_000_003, world=4, rank=3, shapes=None, gdt=torch.float32, std=1e-2,
+        outliers=False, peers="full", out="full", flatten=True),
+    "gpt2s_n8_rank3": dict(
+        desc="GPT-2-small list (148 tensors, 124,439,808 elements), N=8, rank 3, full flat "
+             "replicas; 653 MB per step (partly cache-resident)",
+        numel=None, world=8, rank=3, shapes="gpt2", gdt=torch.bfloat16, std=1e-3,
+        outliers=False, peers="full", out="full", flatten=True),
+    "llama13b_n8_rank7": dict(
+        desc="Llama-13B list + one scalar (364 tensors, 13,015,864,321 elements), N=8, rank 7 "
+             "(odd lo, 7 pad elements); own gradient flattened from the list, peers hold the "
+             "slice only, bf16 output into the full flat buffer; 1% of gradients x100",
+        numel=None, world=8, rank=7, shapes="llama13b", gdt=torch.bfloat16, std=1e-3,
+        outliers=True, peers="slice", out="full", flatten=True),
+    "flat70b_n64_rank0": dict(
+        desc="70e9-element flat vector, N=64, rank 0 shard of 1,093,750,000, slice-only "
+             "replicas and output; flatten not timed (the full own gradient and its flat copy, "
+             "280 GB, do not fit beside the 64 replica slices)",
+        numel=70_000_000_000, world=64, rank=0, shapes=None, gdt=torch.bfloat16, std=1e-3,
+        outliers=False, peers="slice", out="slice", flatten=False),
+}
+DEFAULT_WORKLOAD = "flat7b_n8_rank0"
+
+
+def _shapes(kind):
+    if kind == "gpt2":
+        return synth.gpt2_small_shapes()
+    if kind == "llama13b":
+        return synth.llama_shapes(40, 5120, 13824, trailing_scalar=True)
+    return None
+
+
+def build_inputs(w, dev):
+    """Seeded inputs of a workload, resident on the device: the shard
+    state, this rank's gradient as a tensor list plus its flat buffer, the
+    other ranks' replicas, and the parameter output."""
+    shapes = _shapes(w["shapes"])
+    numel = synth.numel_of(shapes) if shapes else w["numel"]
+    world, rank, gdt = w["world"], w["rank"], w["gdt"]
+    st = zero.ShardState(numel, world, rank, LR, BETAS, EPS)
+    S, lo, P = st.shard, st.lo, st.padded
+    valid = max(0, min(S, numel - lo))
+    p = torch.zeros(S, dtype=torch.float32, device=dev)
+    synth.fill_gaussian(p[:valid], synth.PARAM_STD, synth.PARAM_SEED)
+    st.load_master(p, flat_offset=0)
+    del p
+
+    def grad_fill(buf, q):
+        synth.fill_gaussian(buf, w["std"], synth.grad_seed(1, q),
+                            synth.mask_seed(1, q) if w["outliers"] else None)
+
+    own_tensors, own_flat = None, None
+    if w["flatten"]:
+        storage = torch.empty(numel, dtype=gdt, device=dev)
+        grad_fill(storage, rank)
+        own_tensors = synth.split_views(storage, shapes) if shapes else [storage]
+        own_flat = torch.empty(P, dtype=gdt, device=dev)
+        own = own_flat[lo:lo + S]
+    else:
+        own = torch.zeros(S, dtype=gdt, device=dev)
+        grad_fill(own[:valid], rank)
+    reps = []
+    for q in range(world):
+        if q == rank:
+            reps.append(own)
+            continue
+        if w["peers"] == "full":
+            buf = torch.zeros(P, dtype=gdt, device=dev)
+            grad_fill(buf[lo:lo + valid], q)
+            reps.append(buf[lo:lo + S])
+        else:
+            buf = torch.zeros(S, dtype=gdt, device=dev)
+            grad_fill(buf[:valid], q)
+            reps.append(buf)
+    if w["out"] == "full":
+        out = torch.zeros(P, dtype=torch.bfloat16, device=dev)[lo:lo + S]
+    else:
+        out = torch.zeros(S, dtype=torch.bfloat16, device=dev)
+    return dict(st=st, numel=numel, S=S, lo=lo, P=P, own_tensors=own_tensors,
+                own_flat=own_flat, reps=reps, out=out, ntensors=len(shapes) if shapes else 1)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD,
+                    help="shard to time; the others than the default skip the CPU baseline "
+                         "and the extras")
     ap.add_argument("--cpu-window", type=int, default=1 << 24)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -265,47 +361,40 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     zero.lib()
+    default = args.workload == DEFAULT_WORKLOAD
+    w = WORKLOADS[args.workload]
+    world = w["world"]
+    gsize = torch.tensor([], dtype=w["gdt"]).element_size()
 
-    st = zero.ShardState(NUMEL, WORLD, RANK, LR, BETAS, EPS)
-    S, lo, P = st.shard, st.lo, st.padded
-    log(f"shard={S} lo={lo} padded={P}; generating inputs")
-    p = synth.gaussian(S, synth.PARAM_STD, synth.PARAM_SEED, torch.float32, dev)
-    st.load_master(p, flat_offset=0)
-    del p
-    own_grad = torch.empty(NUMEL, dtype=torch.bfloat16, device=dev)
-    synth.fill_gaussian(own_grad, 1e-3, synth.grad_seed(1, RANK))
-    own_flat = torch.empty(P, dtype=torch.bfloat16, device=dev)
-    peers = []
-    for q in range(WORLD):
-        if q == RANK:
-            continue
-        r = torch.empty(S, dtype=torch.bfloat16, device=dev)
-        synth.fill_gaussian(r, 1e-3, synth.grad_seed(1, q))
-        peers.append(r)
-    reps = peers[:RANK] + [own_flat[lo:lo + S]] + peers[RANK:]
-    params_full = torch.zeros(P, dtype=torch.bfloat16, device=dev)
+    log(f"{args.workload}: generating inputs")
+    inp = build_inputs(w, dev)
+    st, S, lo, P, numel = inp["st"], inp["S"], inp["lo"], inp["P"], inp["numel"]
+    reps, out = inp["reps"], inp["out"]
+    own_tensors, own_flat = inp["own_tensors"], inp["own_flat"]
+    ntensors = inp["ntensors"]
     torch.cuda.synchronize()
-    log("inputs resident; warming up")
+    log(f"shard={S} lo={lo} padded={P}; inputs resident; warming up")
 
     stream = torch.cuda.current_stream()
     n_total = args.warmup + args.steps
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_total)]
-    for i in range(args.warmup):
+
+    def one(i):
         ev[i][0].record(stream)
-        st.flatten([own_grad], own_flat)
+        if own_tensors is not None:
+            st.flatten(own_tensors, own_flat)
         ev[i][1].record(stream)
-        st.step(reps, i + 1, params_full, grad_offset=0, param_offset=lo)
+        st.step(reps, i + 1, out, grad_offset=0, param_offset=0)
         ev[i][2].record(stream)
+
+    for i in range(args.warmup):
+        one(i)
     torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
     t0 = time.perf_counter()
     for i in range(args.warmup, n_total):
-        ev[i][0].record(stream)
-        st.flatten([own_grad], own_flat)
-        ev[i][1].record(stream)
-        st.step(reps, i + 1, params_full, grad_offset=0, param_offset=lo)
-        ev[i][2].record(stream)
+        one(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     flat_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, n_total)])
@@ -313,34 +402,42 @@ def main():
 
     ms_per_step = wall * 1e3 / args.steps
     value = S * args.steps / wall
-    bpe = step_bytes_per_elem(WORLD)
+    bpe = step_bytes_per_elem(world, gsize)
     k2_bytes = bpe * S
-    k1_bytes = 2 * NUMEL + 2 * P
+    k1_bytes = gsize * (numel + P) if own_tensors is not None else 0
     k2_gbps = k2_bytes / (step_ms.mean() * 1e-3) / 1e9
-    k1_gbps = k1_bytes / (flat_ms.mean() * 1e-3) / 1e9
-    traffic = measured_traffic()
+    traffic = measured_traffic() if default else None
 
-    # the step must have produced finite, changing parameters
-    assert torch.isfinite(params_full[:S].float()).all().item()
+    # the step must have produced finite parameters
+    assert torch.isfinite(out[:max(0, min(S, numel - lo))].float()).all().item()
 
     extras = {}
-    if not args.no_extras:
+    if default and not args.no_extras:
         log("bucketed step")
-        extras["bucketed_step_2_streams"] = bucketed_extras(st, reps, params_full, n_total + 1)
+        extras["bucketed_step_2_streams"] = bucketed_extras(st, reps, out, n_total + 1)
 
-    del own_grad, own_flat, peers, reps, params_full
+    del inp, reps, out, own_tensors, own_flat
     st.close()
     torch.cuda.empty_cache()
 
     context = {}
     if not args.no_context:
         context["torch_copy_gbps"] = round(copy_ceiling(8 << 30), 1)
-    if not args.no_extras:
+    if default and not args.no_extras:
         log("tensor-list flatten/unflatten")
         extras["llama7b_list"] = list_extras(dev)
         log("per-parameter (dim-0) layout step")
         extras["fsdp_llama7b_n8_rank0"] = fsdp_extras(dev)
 
+    kernels = {
+        "fused_step": {"ms_mean": float(step_ms.mean()), "ms_min": float(step_ms.min()),
+                       "bytes_per_launch": k2_bytes, "bytes_per_elem": bpe,
+                       "gbps": k2_gbps, "elements_per_s": S / (step_ms.mean() * 1e-3)},
+    }
+    if k1_bytes:
+        kernels["flatten"] = {"ms_mean": float(flat_ms.mean()), "ms_min": float(flat_ms.min()),
+                              "bytes_per_launch": k1_bytes, "tensors": ntensors,
+                              "gbps": k1_bytes / (flat_ms.mean() * 1e-3) / 1e9}
     result = {
         "metric": "sharded Adam step: elements/s and achieved HBM GB/s (% of peak), 7B N=8",
         "value": value,
@@ -352,28 +449,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 (bf16 gradients and parameter output)",
-        "data": "synthetic: seeded N(0,1e-3) bf16 gradients, N(0,0.02) fp32 parameters",
-        "config": {"workload": "flat7b_n8_rank0: 7e9-element flat vector, N=8 simulated "
-                               "ranks, rank 0 shard of 875,000,000",
-                   "numel": NUMEL, "world": WORLD, "rank": RANK, "shard": S,
+        "dtype": "f32 (%s gradients, bf16 parameter output)" % ("bf16" if gsize == 2 else "f32"),
+        "data": "synthetic: seeded N(0,%g) %s gradients, N(0,0.02) fp32 parameters"
+                % (w["std"], "bf16" if gsize == 2 else "fp32"),
+        "config": {"workload": f"{args.workload}: {w['desc']}",
+                   "numel": numel, "world": world, "rank": w["rank"], "shard": S,
                    "parallelism": "zero2-shard, 1 GPU"},
         "step_hbm_gbps": (k1_bytes + k2_bytes) / (ms_per_step * 1e-3) / 1e9,
-        "kernels": {
-            "fused_step": {"ms_mean": float(step_ms.mean()), "ms_min": float(step_ms.min()),
-                           "bytes_per_launch": k2_bytes, "bytes_per_elem": bpe,
-                           "gbps": k2_gbps, "elements_per_s": S / (step_ms.mean() * 1e-3)},
-            "flatten": {"ms_mean": float(flat_ms.mean()), "ms_min": float(flat_ms.min()),
-                        "bytes_per_launch": k1_bytes, "gbps": k1_gbps},
-        },
+        "kernels": kernels,
         "roofline": {"bound": "hbm", "achieved": k2_gbps, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": k2_gbps / PEAK_HBM_GBPS,
                      "traffic": traffic,
-                     "kernel": "fused reduce+Adam+bf16 step (step_vec_kernel<8,bf16,bf16>)"},
+                     "kernel": ("fused reduce+Adam+bf16 step (step_vec_kernel<8,bf16,bf16>)"
+                                if default else "fused reduce+Adam step")},
         "context": context,
         "extras": extras,
     }
-    if not args.no_cpu_baseline:
+    if default and not args.no_cpu_baseline:
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(args.cpu_window, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -28,8 +28,11 @@
  *     caller passes (0 = the null stream). A fault inside a kernel surfaces
  *     at the caller's next synchronisation, not as a return code here.
  *   - Element counts are int64: shards of more than 2^31 elements are fine.
- *   - Misaligned device pointers are accepted (a slower path runs); only
- *     bf16 (2-byte) and fp32 (4-byte) natural alignment is required.
+ *   - Device pointers need only bf16 (2-byte) or fp32 (4-byte) natural
+ *     alignment. The step runs 16-byte vectors whatever the buffers'
+ *     offsets; buffers at different 16-byte phases cost a few percent, and
+ *     shards or ranges shorter than about 16 elements run element by
+ *     element.
  *   - The library owns the context and its master/m/v buffers; the caller
  *     owns every pointer it passes, and its streams.
  *   - Output buffers must not overlap any input of the same call (the
@@ -168,8 +171,8 @@ int zero_step(zero_ctx *ctx, const void *const *grad_replicas,
  * param_out[param_offset + i], for i < count, with the same arithmetic, so
  * covering the shard with disjoint ranges gives results bit-identical to
  * one zero_step. Ranges launched on different streams must be disjoint;
- * the library does not order them. Ranges that start on a multiple of 8
- * elements with 16-byte aligned buffers take the vector path.
+ * the library does not order them. Any range start takes the vector path
+ * after a head of at most 7 elements.
  * EINVAL: as zero_step, plus shard_begin < 0, count < 0 or
  * shard_begin + count > shard. count == 0 is a no-op. */
 int zero_step_range(zero_ctx *ctx, int64_t shard_begin, int64_t count,

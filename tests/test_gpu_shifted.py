@@ -1,0 +1,108 @@
+"""Buffers at mixed 16-byte phases: the shifted vector path.
+
+The state's phase is fixed by the library (lo mod 4 elements past a 256-byte
+boundary); replicas and output here sit at every element phase relative to
+it, each replica at its own phase. Every combination must give the oracle's
+values bit for bit, and the output must touch exactly its own elements
+(sentinels before and after the output view stay intact)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import zero_partitioned_optimizer_flatten_amd as zero
+from gpu_harness import assert_bitexact_state, assert_state_parity, bits, gpu_state, log
+
+pytestmark = pytest.mark.gpu
+LR, BETAS, EPS = 1e-3, (0.9, 0.999), 1e-8
+SENTINEL = -1                      # 0xFFFF in bf16 bits, NaN pattern 0xFFFFFFFF in fp32
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available()
+    zero.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _elems_per_16b(dtype):
+    return 16 // torch.tensor([], dtype=dtype).element_size()
+
+
+def _run_phases(world, rank, S, gdt, odt, combos, label):
+    """One shard state; step t uses the t-th (replica offsets, output offset)
+    combination, each replica a view at that element offset into a fresh
+    allocation."""
+    dev = torch.device("cuda")
+    numel = world * S - (1 if world > 1 else 0)
+    st = zero.ShardState(numel, world, rank, LR, BETAS, EPS)
+    assert st.shard == S
+    orc = oracle.ShardOracle(numel, world, rank, LR, BETAS, EPS)
+    valid = max(0, min(S, numel - st.lo))
+    p = torch.zeros(S, dtype=torch.float32, device=dev)
+    p[:valid] = synth.gaussian(valid, synth.PARAM_STD, synth.PARAM_SEED + rank, torch.float32, dev)
+    st.load_master(p, flat_offset=0)
+    orc.master[:] = bits(p)
+    ivt = torch.int16 if odt == torch.bfloat16 else torch.int32
+    for t, (roffs, ooff) in enumerate(combos, start=1):
+        reps, reps_h = [], []
+        for q in range(world):
+            buf = torch.zeros(S + 16, dtype=gdt, device=dev)
+            g = buf[roffs[q]:roffs[q] + S]
+            g[:valid] = synth.gaussian(valid, 1e-3, synth.grad_seed(t, q), gdt, dev)
+            reps.append(g)
+            reps_h.append(bits(g))
+        obuf = torch.full((S + 16,), SENTINEL, dtype=ivt, device=dev).view(odt)
+        out = obuf[ooff:ooff + S]
+        st.step(reps, t, out)
+        out_ref = np.zeros(S, np.uint16 if odt == torch.bfloat16 else np.float32)
+        orc.step(reps_h, t, out_ref, grad_offset=0, out_offset=0)
+        torch.cuda.synchronize()
+        whole = obuf.view(ivt).cpu().numpy()
+        assert np.all(whole[:ooff] == SENTINEL) and np.all(whole[ooff + S:] == SENTINEL), \
+            f"{label} t={t}: output store left its view (offset {ooff})"
+        got = bits(out)
+        tag = f"{label} t={t} reps@{list(roffs)} out@{ooff}"
+        assert_bitexact_state(tag, gpu_state(st), [orc.master, orc.m, orc.v], got, out_ref)
+    assert_state_parity(label, gpu_state(st), [orc.master, orc.m, orc.v])
+    st.close()
+
+
+@pytest.mark.parametrize("gdt,odt", [(torch.bfloat16, torch.bfloat16),
+                                     (torch.bfloat16, torch.float32),
+                                     (torch.float32, torch.bfloat16),
+                                     (torch.float32, torch.float32)])
+def test_every_phase_against_every_state_shift(gdt, odt):
+    """N = 4, S = 5001 (= 1 mod 4, so rank r's state sits r elements past a
+    16-byte boundary), ranks 0..3; for each, all 8 replica base phases
+    (replica q at (base + 3q) mod 8) against all 8 output phases."""
+    S, world = 5001, 4
+    combos = [(tuple((rp + 3 * q) % 8 for q in range(world)), op)
+              for rp in range(8) for op in range(8)]
+    for rank in range(world):
+        _run_phases(world, rank, S, gdt, odt, combos, f"phases N=4 r{rank} {gdt}->{odt}")
+
+
+@pytest.mark.parametrize("world", [1, 2, 3, 8, 16, 64])
+def test_phases_every_compiled_replica_count(world):
+    """Each compiled replica count (and the runtime-N kernel at N = 3) on
+    the shifted path: bf16 replicas at mixed phases, bf16 output."""
+    S = 4097
+    rng = np.random.default_rng(world)
+    combos = [(tuple(int(x) for x in rng.integers(0, 8, world)), int(rng.integers(0, 8)))
+              for _ in range(6)]
+    combos.append((tuple([1] * world), 0))
+    combos.append((tuple([0] * world), 7))
+    rank = world - 1
+    _run_phases(world, rank, S, torch.bfloat16, torch.bfloat16, combos,
+                f"phases N={world} r{rank}")
+
+
+def test_shifted_path_short_shards():
+    """Shards of 8..40 elements: head, at most a few vectors, tail."""
+    for S in (8, 9, 15, 16, 17, 23, 40):
+        combos = [((1, 2), 3), ((0, 5), 0), ((7, 7), 6)]
+        _run_phases(2, 1, S, torch.bfloat16, torch.bfloat16, combos, f"short S={S}")
+        log(f"short shard S={S} ok")

@@ -317,6 +317,258 @@ step_elem_kernel(Reps<0> reps, int nrep, float *__restrict__ master,
         step_one<0, GB, PB>(reps, nrep, master, mom, var, out, i, sc);
 }
 
+// ------------------------------------------------------ shifted vector path
+// For caller buffers that do not share one 16-byte phase with the state
+// (e.g. replicas holding only this rank's slice next to a full flat output
+// at an odd offset lo). The vector partition follows the state, so master,
+// m and v keep their aligned 16-byte accesses.
+//
+// A bf16 replica whose vector j starts d elements past a 16-byte boundary
+// spans aligned blocks j and j+1 of its aligned base. Each lane loads block
+// j; block j+1 is the next lane's block j, taken across lanes (DPP wave
+// shift), so a wavefront still issues one 16-byte load per lane per
+// replica (measured 10-15% faster than loading both blocks in every lane).
+// The wave's last lane and the lane of the last vector load block j+1
+// themselves; that block holds at least one of the lane's own elements, so
+// no read leaves the 16-byte blocks of the buffer's own elements.
+//
+// An output at another phase is written with 2-, 4- and 8-byte stores that
+// cover exactly the lane's elements (measured no slower than a cross-lane
+// realignment into whole blocks). fp32 replicas read the three aligned
+// blocks that cover a lane's 32 bytes.
+
+// Replica pointer table: each base 16-byte aligned, and d[q] the number of
+// elements between it and the replica's element 0 of the vector range.
+template <int NR>
+struct ShiftReps {
+    const void *p[NR > 0 ? NR : ZERO_MAX_WORLD];
+    uint8_t d[NR > 0 ? NR : ZERO_MAX_WORLD];
+};
+
+// Value of v in the next lane of the wavefront (DPP wave shift left by one;
+// lanes without a next lane get 0 and do not use it).
+__device__ __forceinline__ uint32_t next_lane(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, false);
+}
+
+__device__ __forceinline__ uint4 next_lane(uint4 v) {
+    return make_uint4(next_lane(v.x), next_lane(v.y), next_lane(v.z), next_lane(v.w));
+}
+
+template <bool GB> struct ShiftRaw;
+template <> struct ShiftRaw<true> { uint4 a, b; };             // blocks j, j+1 (8 bf16 each)
+template <> struct ShiftRaw<false> { float4 a, b, c; };        // 3 blocks of 4 fp32
+
+__device__ __forceinline__ ShiftRaw<true> load_shift(const void *base, int d, int64_t j,
+                                                     bool self_next, ShiftRaw<true> *) {
+    const uint4 *p = reinterpret_cast<const uint4 *>(base) + j;
+    ShiftRaw<true> r;
+    r.a = ld_u4<ZK_NT_GRAD>(p);
+    r.b = make_uint4(0u, 0u, 0u, 0u);
+    if (d && self_next) r.b = ld_u4<ZK_NT_GRAD>(p + 1);
+    return r;
+}
+
+__device__ __forceinline__ ShiftRaw<false> load_shift(const void *base, int d, int64_t j,
+                                                      bool, ShiftRaw<false> *) {
+    const float4 *p = reinterpret_cast<const float4 *>(base) + 2 * j;
+    ShiftRaw<false> r;
+    r.a = ld_f4<ZK_NT_GRAD>(p);
+    r.b = ld_f4<ZK_NT_GRAD>(p + 1);
+    r.c = d ? ld_f4<ZK_NT_GRAD>(p + 2) : make_float4(0.f, 0.f, 0.f, 0.f);
+    return r;
+}
+
+// Block j+1 from the next lane, for the lanes that did not load it.
+__device__ __forceinline__ void complete_shift(ShiftRaw<true> &r, int d, bool self_next) {
+    if (!d) return;
+    const uint4 nb = next_lane(r.a);
+    if (!self_next) r.b = nb;
+}
+
+__device__ __forceinline__ void complete_shift(ShiftRaw<false> &, int, bool) {}
+
+// Four words (eight bf16) starting D elements into the 16 elements of c:
+// word k is bytes [2D + 4k, 2D + 4k + 4).
+template <int D>
+__device__ __forceinline__ uint4 take_words(const uint32_t (&c)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        w[k] = (D % 2 == 0) ? c[k + D / 2]
+                            : __builtin_amdgcn_alignbyte(c[k + D / 2 + 1], c[k + D / 2], 2);
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint4 take_words(const uint32_t (&c)[8], int d) {
+    switch (d) {
+    case 0: return take_words<0>(c);
+    case 1: return take_words<1>(c);
+    case 2: return take_words<2>(c);
+    case 3: return take_words<3>(c);
+    case 4: return take_words<4>(c);
+    case 5: return take_words<5>(c);
+    case 6: return take_words<6>(c);
+    default: return take_words<7>(c);
+    }
+}
+
+__device__ __forceinline__ void unpack_shift(const ShiftRaw<true> &r, int d, float (&x)[kVec]) {
+    const uint32_t c[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
+    RawVec<true> v;
+    v.a = take_words(c, d);
+    unpack(v, x);
+}
+
+template <int D>
+__device__ __forceinline__ void take_f32(const float (&c)[12], float (&x)[kVec]) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) x[e] = c[D + e];
+}
+
+__device__ __forceinline__ void unpack_shift(const ShiftRaw<false> &r, int d, float (&x)[kVec]) {
+    const float c[12] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y,
+                         r.b.z, r.b.w, r.c.x, r.c.y, r.c.z, r.c.w};
+    switch (d) {
+    case 0: take_f32<0>(c, x); break;
+    case 1: take_f32<1>(c, x); break;
+    case 2: take_f32<2>(c, x); break;
+    default: take_f32<3>(c, x); break;
+    }
+}
+
+template <int NR, bool GB>
+__device__ __forceinline__ void fold_group_shift(const ShiftReps<NR> &reps, int q0, int n,
+                                                 int64_t j, bool self_next, float (&s)[kVec]) {
+    ShiftRaw<GB> raw[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k)
+        if (q0 + k < n)
+            raw[k] = load_shift(reps.p[q0 + k], reps.d[q0 + k], j, self_next,
+                                (ShiftRaw<GB> *)nullptr);
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        if (q0 + k < n) {
+            complete_shift(raw[k], reps.d[q0 + k], self_next);
+            float x[kVec];
+            unpack_shift(raw[k], reps.d[q0 + k], x);
+            if (q0 + k == 0) {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) s[e] = x[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) s[e] = s[e] + x[e];
+            }
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void st_nt(T *p, T v) {
+    if (ZK_NT_OUT) __builtin_nontemporal_store(v, p);
+    else *p = v;
+}
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Eight packed bf16 values (o.x = elements 0,1, ...) to q, which sits
+// d elements past a 16-byte boundary.
+__device__ __forceinline__ void store_bf16x8_at(uint16_t *q, int d, uint4 o) {
+    if (d == 0) {
+        st_u4<ZK_NT_OUT>(q, o);
+    } else if (d == 4) {                                 // 8-byte aligned
+        st_nt(reinterpret_cast<u32x2_t *>(q), u32x2_t{o.x, o.y});
+        st_nt(reinterpret_cast<u32x2_t *>(q + 4), u32x2_t{o.z, o.w});
+    } else if ((d & 1) == 0) {                           // 4-byte aligned
+        uint32_t *w = reinterpret_cast<uint32_t *>(q);
+        st_nt(w, o.x);
+        st_nt(w + 1, o.y);
+        st_nt(w + 2, o.z);
+        st_nt(w + 3, o.w);
+    } else {                                             // 2 mod 4: q + 1 is 4-byte aligned
+        uint32_t *w = reinterpret_cast<uint32_t *>(q + 1);
+        st_nt(q, (uint16_t)(o.x & 0xFFFFu));
+        st_nt(w, __builtin_amdgcn_alignbyte(o.y, o.x, 2));
+        st_nt(w + 1, __builtin_amdgcn_alignbyte(o.z, o.y, 2));
+        st_nt(w + 2, __builtin_amdgcn_alignbyte(o.w, o.z, 2));
+        st_nt(q + 7, (uint16_t)(o.w >> 16));
+    }
+}
+
+// Eight fp32 values to q, which sits d elements past a 16-byte boundary.
+__device__ __forceinline__ void store_f32x8_at(float *q, int d, const float (&x)[kVec]) {
+    if (d == 0) {
+        st_f4<ZK_NT_OUT>(q, make_float4(x[0], x[1], x[2], x[3]));
+        st_f4<ZK_NT_OUT>(q + 4, make_float4(x[4], x[5], x[6], x[7]));
+    } else if (d == 2) {                                 // 8-byte aligned
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            st_nt(reinterpret_cast<f32x2_t *>(q + 2 * k), f32x2_t{x[2 * k], x[2 * k + 1]});
+    } else {                                             // q + 1 is 8-byte aligned
+        st_nt(q, x[0]);
+#pragma unroll
+        for (int k = 0; k < 3; ++k)
+            st_nt(reinterpret_cast<f32x2_t *>(q + 1 + 2 * k), f32x2_t{x[1 + 2 * k], x[2 + 2 * k]});
+        st_nt(q + 7, x[7]);
+    }
+}
+
+// Vector j of the shifted path: state aligned; replicas read through
+// their aligned bases; the output (element pointer of the range's first
+// element, dout elements past a 16-byte boundary) written at its phase.
+template <int NR, bool GB, bool PB>
+__global__ void __launch_bounds__(kBlock)
+step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
+                  float *__restrict__ mom, float *__restrict__ var, void *__restrict__ out,
+                  int dout, int64_t nvec, StepScalars sc) {
+    const int n = NR > 0 ? NR : nrep;
+    constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
+    const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
+    const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+    if (j >= nvec) return;
+    const bool self_next = (threadIdx.x % 64) == 63 || j + 1 == nvec;
+    float p[kVec], m[kVec], v[kVec];
+    load8(master, j, p);
+    load8(mom, j, m);
+    load8(var, j, v);
+
+    float s[kVec];
+    if constexpr (NR > 0 && NR <= 2 * kGroup) {
+#pragma unroll
+        for (int q0 = 0; q0 < NR; q0 += kGroup)
+            fold_group_shift<NR, GB>(reps, q0, n, j, self_next, s);
+    } else {
+#pragma unroll 1
+        for (int q0 = 0; q0 < n; q0 += kGroup)
+            fold_group_shift<NR, GB>(reps, q0, n, j, self_next, s);
+    }
+    float g[kVec];
+    if (pow2) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;
+    } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
+    }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
+
+    store8<false>(master, j, p);
+    store8<false>(mom, j, m);
+    store8<false>(var, j, v);
+    if (PB) {
+        uint4 o;
+        o.x = round_bf16(p[0]) | (round_bf16(p[1]) << 16);
+        o.y = round_bf16(p[2]) | (round_bf16(p[3]) << 16);
+        o.z = round_bf16(p[4]) | (round_bf16(p[5]) << 16);
+        o.w = round_bf16(p[6]) | (round_bf16(p[7]) << 16);
+        store_bf16x8_at(reinterpret_cast<uint16_t *>(out) + kVec * j, dout, o);
+    } else {
+        store_f32x8_at(reinterpret_cast<float *>(out) + kVec * j, dout, p);
+    }
+}
+
 // ------------------------------------------------ per-parameter (dim-0) layout
 // Each segment is one parameter's local row shard: its replica pointers
 // (already at this rank's first row), its output shard, and its place in
@@ -461,13 +713,92 @@ inline int common_head(const StepArgs &a) {
     return -1;
 }
 
+// Head for the shifted path: the h in [0, 8) at which master, m and v are
+// 16-byte aligned and the most caller streams are too (the output counts
+// double: its unaligned form costs more instructions than a replica's), or
+// -1 if no h aligns the state or a buffer is not naturally aligned.
+inline int shifted_head(const StepArgs &a) {
+    const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
+    if ((uintptr_t)a.out % oe) return -1;
+    for (int q = 0; q < a.n; ++q)
+        if ((uintptr_t)a.grads[q] % ge) return -1;
+    int best = -1, best_score = -1;
+    for (int h = 0; h < kVec; ++h) {
+        if (((uintptr_t)a.master + 4u * h) % 16 || ((uintptr_t)a.m + 4u * h) % 16 ||
+            ((uintptr_t)a.v + 4u * h) % 16)
+            continue;
+        int score = ((uintptr_t)a.out + (uintptr_t)oe * h) % 16 == 0 ? 2 : 0;
+        for (int q = 0; q < a.n; ++q) score += ((uintptr_t)a.grads[q] + (uintptr_t)ge * h) % 16 == 0;
+        if (score > best_score) {
+            best = h;
+            best_score = score;
+        }
+    }
+    return best;
+}
+
+template <int NR, bool GB, bool PB>
+hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stream) {
+    const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
+    ShiftReps<NR> reps;
+    for (int q = 0; q < a.n; ++q) {
+        const uintptr_t e0 = (uintptr_t)a.grads[q] + (uintptr_t)ge * h;
+        reps.d[q] = (uint8_t)((e0 % 16) / ge);
+        reps.p[q] = (const void *)(e0 - e0 % 16);
+    }
+    void *out = (char *)a.out + (int64_t)oe * h;
+    const int dout = (int)(((uintptr_t)out % 16) / oe);
+    const int64_t grid = (nvec + kBlock - 1) / kBlock;
+    if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((step_shift_kernel<NR, GB, PB>), dim3((unsigned)grid), dim3(kBlock),
+                       ZK_STEP_LDS, stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
+                       nvec, a.sc);
+    return hipGetLastError();
+}
+
+template <bool GB, bool PB>
+hipError_t dispatch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stream) {
+    switch (a.n) {
+    case 1: return launch_shift<1, GB, PB>(a, h, nvec, stream);
+    case 2: return launch_shift<2, GB, PB>(a, h, nvec, stream);
+    case 4: return launch_shift<4, GB, PB>(a, h, nvec, stream);
+    case 8: return launch_shift<8, GB, PB>(a, h, nvec, stream);
+    case 16: return launch_shift<16, GB, PB>(a, h, nvec, stream);
+    case 64: return launch_shift<64, GB, PB>(a, h, nvec, stream);
+    default: return launch_shift<0, GB, PB>(a, h, nvec, stream);
+    }
+}
+
+// Element head [0, h), vector range, element tail.
+template <bool GB, bool PB>
+hipError_t step_shifted(const StepArgs &a, int h, hipStream_t stream) {
+    const int64_t nvec = (a.shard - h) / kVec;
+    if (h > 0) {
+        hipError_t e = launch_elem<GB, PB>(a, 0, h, stream);
+        if (e != hipSuccess) return e;
+    }
+    hipError_t e = dispatch_shift<GB, PB>(a, h, nvec, stream);
+    if (e != hipSuccess) return e;
+    const int64_t done = h + nvec * kVec;
+    if (done < a.shard) return launch_elem<GB, PB>(a, done, a.shard, stream);
+    return hipSuccess;
+}
+
 template <bool GB, bool PB>
 hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     // Vector path from the first element at which all streams are 16-byte
     // aligned; the few elements before it and the ragged tail take the
-    // element path (same arithmetic).
+    // element path (same arithmetic). Buffers at mixed phases take the
+    // shifted vector path; only buffers that are not naturally aligned, or
+    // shards shorter than the head plus one vector, run on the element path
+    // alone.
     const int h = common_head(a);
-    if (h < 0 || a.shard - h < kVec) return launch_elem<GB, PB>(a, 0, a.shard, stream);
+    if (h < 0) {
+        const int hs = shifted_head(a);
+        if (hs >= 0 && a.shard - hs >= kVec) return step_shifted<GB, PB>(a, hs, stream);
+        return launch_elem<GB, PB>(a, 0, a.shard, stream);
+    }
+    if (a.shard - h < kVec) return launch_elem<GB, PB>(a, 0, a.shard, stream);
     const int64_t nvec = (a.shard - h) / kVec;
     if (h > 0) {
         hipError_t e = launch_elem<GB, PB>(a, 0, h, stream);
