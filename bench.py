@@ -168,6 +168,39 @@ def bucketed_extras(st, reps, out, t0, sizes=(1 << 22, 1 << 24, 1 << 26), nstrea
     return res
 
 
+def bucketed_graph_extras(st, reps, out, t0, sizes=(1 << 20, 1 << 22, 1 << 24),
+                          nstreams=(1, 2)):
+    """The bucketed step with the step count on the device: step_begin plus
+    one step_range_sched per bucket, captured once as a HIP graph and
+    replayed (each replay is one whole step); with 2 streams, buckets
+    alternate between two branches of the graph after step_begin."""
+    S = st.shard
+    st.schedule(t0)
+    res = {}
+    for ns in nstreams:
+        for bucket in sizes:
+            g = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            with torch.cuda.graph(g):
+                cur = torch.cuda.current_stream()
+                st.step_begin()
+                streams = [cur] + ([side] if ns > 1 else [])
+                if ns > 1:
+                    side.wait_stream(cur)
+                for i, b0 in enumerate(range(0, S, bucket)):
+                    cnt = min(bucket, S - b0)
+                    st.step_range_sched(b0, cnt, [r[b0:] for r in reps], out, grad_offset=0,
+                                        param_offset=b0, stream=streams[i % ns])
+                if ns > 1:
+                    cur.wait_stream(side)
+            ms = _time_ms(g.replay, reps=3)
+            res[f"{bucket}x{ns}"] = {"buckets": (S + bucket - 1) // bucket, "streams": ns,
+                                     "ms": ms,
+                                     "gbps": step_bytes_per_elem(WORLD) * S / (ms * 1e-3) / 1e9}
+            del g
+    return res
+
+
 def list_extras(dev):
     """Multi-tensor flatten and unflatten on the Llama-7B-shaped list
     (291 tensors, 6,738,415,616 bf16 elements)."""
@@ -414,7 +447,10 @@ def main():
     extras = {}
     if default and not args.no_extras:
         log("bucketed step")
-        extras["bucketed_step_2_streams"] = bucketed_extras(st, reps, out, n_total + 1)
+        extras["bucketed_step_2_streams"] = bucketed_extras(
+            st, reps, out, n_total + 1, sizes=(1 << 20, 1 << 22, 1 << 24, 1 << 26))
+        log("bucketed step, graph replay")
+        extras["bucketed_step_graph"] = bucketed_graph_extras(st, reps, out, n_total + 100)
 
     del inp, reps, out, own_tensors, own_flat
     st.close()

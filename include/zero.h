@@ -236,6 +236,67 @@ int zero_fsdp_step(zero_ctx *ctx, const void *const *grads, int32_t n_replicas,
                    zero_dtype grad_dtype, void *const *params_out,
                    zero_dtype param_dtype, int64_t t, hipStream_t stream);
 
+/* ---- Device-resident step schedule (graph-replayable steps) ----------
+ * The step count t and the learning rate can live in device memory, so a
+ * captured HIP graph of a step replays as successive steps ([ZeRO and
+ * FSDP], "Implementing ZeRO's Adam from scratch": ZeroAdam keeps its own
+ * step count and increments it on every step). The scheduled calls below
+ * take t and lr from the device instead of their arguments; their
+ * arithmetic, and so their results, equal zero_step's at that t and lr bit
+ * for bit: the bias corrections come from a table the library builds on
+ * the host at zero_schedule_init exactly as it forms them for a host t.
+ * Between zero_schedule_init and zero_destroy the scheduled calls launch
+ * kernels only (no allocation, no memset, no host synchronisation), so
+ * they can be recorded by HIP stream capture. */
+
+/* Longest bias-correction table (in steps) the schedule accepts; betas for
+ * which 1 - b^t has not reached 1 in binary32 by then are EUNSUPPORTED. */
+#define ZERO_SCHEDULE_MAX_TABLE (1 << 22)
+
+/* Create the schedule if the context has none (device allocation and a
+ * synchronous upload: not capturable), then set, stream-ordered, the next
+ * step count to next_t and the device learning rate to the context's lr.
+ * EINVAL: next_t < 1. EUNSUPPORTED: see ZERO_SCHEDULE_MAX_TABLE. */
+int zero_schedule_init(zero_ctx *ctx, int64_t next_t, hipStream_t stream);
+
+/* Set the learning rate of later scheduled steps (stream-ordered; also the
+ * context's host lr). A captured graph takes the lr the device holds when
+ * it replays. EINVAL: no schedule, lr not finite. */
+int zero_schedule_lr(zero_ctx *ctx, double lr, hipStream_t stream);
+
+/* Read back the next step count (waits for `stream`; not capturable), for
+ * checkpoints. EINVAL: no schedule or null output. */
+int zero_schedule_get(const zero_ctx *ctx, int64_t *next_t, hipStream_t stream);
+
+/* Begin the schedule's next step: resolve its scalars on the device and
+ * advance the step count by one. One single-lane kernel. */
+int zero_step_begin(zero_ctx *ctx, hipStream_t stream);
+
+/* zero_step_begin followed by zero_step at the step just begun. Arguments,
+ * checks and errors as zero_step, without t; EINVAL also without a
+ * schedule. */
+int zero_step_sched(zero_ctx *ctx, const void *const *grad_replicas,
+                    int32_t n_replicas, zero_dtype grad_dtype,
+                    int64_t grad_offset, void *param_out,
+                    zero_dtype param_dtype, int64_t param_offset,
+                    hipStream_t stream);
+
+/* zero_step_range at the schedule's current step (the one the last
+ * zero_step_begin began); covering the shard with disjoint ranges after
+ * one zero_step_begin equals one zero_step_sched. */
+int zero_step_range_sched(zero_ctx *ctx, int64_t shard_begin, int64_t count,
+                          const void *const *grad_replicas,
+                          int32_t n_replicas, zero_dtype grad_dtype,
+                          int64_t grad_offset, void *param_out,
+                          zero_dtype param_dtype, int64_t param_offset,
+                          hipStream_t stream);
+
+/* zero_step_begin followed by zero_fsdp_step at the step just begun. */
+int zero_fsdp_step_sched(zero_ctx *ctx, const void *const *grads,
+                         int32_t n_replicas, zero_dtype grad_dtype,
+                         void *const *params_out, zero_dtype param_dtype,
+                         hipStream_t stream);
+
 /* Copy the fp32 state out of / into the context (checkpoint and resume).
  * master, m, v: device pointers to `shard` floats each; any may be NULL to
  * skip that buffer. Stream-ordered device-to-device copies. */

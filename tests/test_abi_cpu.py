@@ -106,6 +106,13 @@ def test_null_context_calls_are_rejected():
     assert L.zero_flatten(None, None, None, 1, 0, None, None) == zero.ZERO_EINVAL
     assert L.zero_get_state(None, None, None, None, None) == zero.ZERO_EINVAL
     assert L.zero_set_lr(None, 1e-3) == zero.ZERO_EINVAL
+    assert L.zero_schedule_init(None, 1, None) == zero.ZERO_EINVAL
+    assert L.zero_schedule_lr(None, 1e-3, None) == zero.ZERO_EINVAL
+    assert L.zero_schedule_get(None, None, None) == zero.ZERO_EINVAL
+    assert L.zero_step_begin(None, None) == zero.ZERO_EINVAL
+    assert L.zero_step_sched(None, None, 4, 1, 0, None, 1, 0, None) == zero.ZERO_EINVAL
+    assert L.zero_step_range_sched(None, 0, 1, None, 4, 1, 0, None, 1, 0, None) == zero.ZERO_EINVAL
+    assert L.zero_fsdp_step_sched(None, None, 4, 1, None, 1, None) == zero.ZERO_EINVAL
     L.zero_destroy(None)
 
 

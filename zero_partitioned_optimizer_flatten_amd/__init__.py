@@ -68,6 +68,14 @@ def lib():
     L.zero_fsdp_local.argtypes = [vp, i32, p64, p64, p64]
     L.zero_fsdp_load_master.argtypes = [vp, vp, ctypes.c_int, vp]
     L.zero_fsdp_step.argtypes = [vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, i64, vp]
+    L.zero_schedule_init.argtypes = [vp, i64, vp]
+    L.zero_schedule_lr.argtypes = [vp, dbl, vp]
+    L.zero_schedule_get.argtypes = [vp, p64, vp]
+    L.zero_step_begin.argtypes = [vp, vp]
+    L.zero_step_sched.argtypes = [vp, vp, i32, ctypes.c_int, i64, vp, ctypes.c_int, i64, vp]
+    L.zero_step_range_sched.argtypes = [vp, i64, i64, vp, i32, ctypes.c_int, i64, vp,
+                                        ctypes.c_int, i64, vp]
+    L.zero_fsdp_step_sched.argtypes = [vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, vp]
     L.zero_get_state.argtypes = [vp, vp, vp, vp, vp]
     L.zero_set_state.argtypes = [vp, vp, vp, vp, vp]
     L.zero_state_bytes.argtypes = [i32, dbl, dbl, ctypes.POINTER(dbl)]
@@ -123,7 +131,8 @@ class ShardState:
     Mirrors the pages' ZeroAdam(params, lr, betas, eps) for one rank: the
     library owns fp32 master/m/v of `shard` elements; gradients, flat
     buffers and streams belong to the caller. The step number t is passed
-    explicitly (first step t = 1).
+    explicitly (first step t = 1), or kept on the device with schedule()
+    for the *_sched calls, which a captured HIP graph can replay.
     """
 
     def __init__(self, numel: int, world: int, rank: int, lr: float,
@@ -224,12 +233,7 @@ class ShardState:
         _check(lib().zero_unflatten(self._h, flat.data_ptr(), len(tensors), numels,
                                     _dtype_code(dt), ptrs, _stream_handle(stream)))
 
-    def step(self, replicas: Sequence[torch.Tensor], t: int, param_out: torch.Tensor,
-             grad_offset: Optional[int] = None, param_offset: Optional[int] = None,
-             stream=None):
-        """One shard step. replicas[q][grad_offset + i] is rank q's gradient of
-        slice element i; writes param_out[param_offset + i]. Offsets default
-        to lo for full padded buffers and 0 for slice-sized ones."""
+    def _step_args(self, replicas, param_out, grad_offset, param_offset):
         if len(replicas) != self.world:
             raise ValueError(f"need {self.world} replicas, got {len(replicas)}")
         gdt = replicas[0].dtype
@@ -248,18 +252,9 @@ class ShardState:
         self._dev(param_out, "param_out")
         if param_out.numel() < po + self.shard:
             raise ValueError(f"param_out has {param_out.numel()} elements, need {po + self.shard}")
-        ptrs = _ptr_array([r.data_ptr() for r in replicas])
-        _check(lib().zero_step(self._h, ptrs, len(replicas), _dtype_code(gdt), go,
-                               param_out.data_ptr(), _dtype_code(param_out.dtype), po,
-                               int(t), _stream_handle(stream)))
+        return _ptr_array([r.data_ptr() for r in replicas]), gdt, int(go), int(po)
 
-    def step_range(self, shard_begin: int, count: int, replicas: Sequence[torch.Tensor],
-                   t: int, param_out: torch.Tensor, grad_offset: int = 0,
-                   param_offset: int = 0, stream=None):
-        """The step on shard elements [shard_begin, shard_begin+count):
-        replicas[q][grad_offset + i] feeds element shard_begin + i, which is
-        written to param_out[param_offset + i]. Disjoint ranges on different
-        streams may run concurrently."""
+    def _range_args(self, shard_begin, count, replicas, param_out, grad_offset, param_offset):
         if len(replicas) != self.world:
             raise ValueError(f"need {self.world} replicas, got {len(replicas)}")
         if shard_begin < 0 or count < 0 or shard_begin + count > self.shard:
@@ -274,11 +269,74 @@ class ShardState:
         self._dev(param_out, "param_out")
         if param_out.numel() < param_offset + count:
             raise ValueError(f"param_out has {param_out.numel()} elements, need {param_offset + count}")
-        ptrs = _ptr_array([r.data_ptr() for r in replicas])
+        return _ptr_array([r.data_ptr() for r in replicas]), gdt
+
+    def step(self, replicas: Sequence[torch.Tensor], t: int, param_out: torch.Tensor,
+             grad_offset: Optional[int] = None, param_offset: Optional[int] = None,
+             stream=None):
+        """One shard step. replicas[q][grad_offset + i] is rank q's gradient of
+        slice element i; writes param_out[param_offset + i]. Offsets default
+        to lo for full padded buffers and 0 for slice-sized ones."""
+        ptrs, gdt, go, po = self._step_args(replicas, param_out, grad_offset, param_offset)
+        _check(lib().zero_step(self._h, ptrs, len(replicas), _dtype_code(gdt), go,
+                               param_out.data_ptr(), _dtype_code(param_out.dtype), po,
+                               int(t), _stream_handle(stream)))
+
+    def step_range(self, shard_begin: int, count: int, replicas: Sequence[torch.Tensor],
+                   t: int, param_out: torch.Tensor, grad_offset: int = 0,
+                   param_offset: int = 0, stream=None):
+        """The step on shard elements [shard_begin, shard_begin+count):
+        replicas[q][grad_offset + i] feeds element shard_begin + i, which is
+        written to param_out[param_offset + i]. Disjoint ranges on different
+        streams may run concurrently."""
+        ptrs, gdt = self._range_args(shard_begin, count, replicas, param_out, grad_offset,
+                                     param_offset)
         _check(lib().zero_step_range(self._h, int(shard_begin), int(count), ptrs, len(replicas),
                                      _dtype_code(gdt), int(grad_offset), param_out.data_ptr(),
                                      _dtype_code(param_out.dtype), int(param_offset), int(t),
                                      _stream_handle(stream)))
+
+    # ------------------------------------------- device-resident schedule
+    def schedule(self, next_t: int = 1, stream=None):
+        """Keep the step count and lr on the device (created on first use,
+        outside any graph capture): the next scheduled step is next_t."""
+        with torch.cuda.device(self.device):
+            _check(lib().zero_schedule_init(self._h, int(next_t), _stream_handle(stream)))
+
+    def schedule_lr(self, lr: float, stream=None):
+        """Learning rate of later scheduled steps (stream-ordered)."""
+        _check(lib().zero_schedule_lr(self._h, float(lr), _stream_handle(stream)))
+
+    def schedule_next_t(self, stream=None) -> int:
+        """The next scheduled step count (waits for the stream)."""
+        out = ctypes.c_int64()
+        _check(lib().zero_schedule_get(self._h, ctypes.byref(out), _stream_handle(stream)))
+        return out.value
+
+    def step_begin(self, stream=None):
+        """Begin the next scheduled step (before step_range_sched calls)."""
+        _check(lib().zero_step_begin(self._h, _stream_handle(stream)))
+
+    def step_sched(self, replicas: Sequence[torch.Tensor], param_out: torch.Tensor,
+                   grad_offset: Optional[int] = None, param_offset: Optional[int] = None,
+                   stream=None):
+        """step() at the device schedule's next step count and lr; advances
+        the count. Capturable in a HIP graph."""
+        ptrs, gdt, go, po = self._step_args(replicas, param_out, grad_offset, param_offset)
+        _check(lib().zero_step_sched(self._h, ptrs, len(replicas), _dtype_code(gdt), go,
+                                     param_out.data_ptr(), _dtype_code(param_out.dtype), po,
+                                     _stream_handle(stream)))
+
+    def step_range_sched(self, shard_begin: int, count: int, replicas: Sequence[torch.Tensor],
+                         param_out: torch.Tensor, grad_offset: int = 0, param_offset: int = 0,
+                         stream=None):
+        """step_range() at the step the last step_begin began."""
+        ptrs, gdt = self._range_args(shard_begin, count, replicas, param_out, grad_offset,
+                                     param_offset)
+        _check(lib().zero_step_range_sched(self._h, int(shard_begin), int(count), ptrs,
+                                           len(replicas), _dtype_code(gdt), int(grad_offset),
+                                           param_out.data_ptr(), _dtype_code(param_out.dtype),
+                                           int(param_offset), _stream_handle(stream)))
 
     def bucket_ranges(self, bucket_bounds: Sequence[int]) -> List[Tuple[int, int, int, int]]:
         """For gradient buckets given as flat-vector boundaries
@@ -378,10 +436,7 @@ class FsdpShardState(ShardState):
         _check(lib().zero_fsdp_load_master(self._h, ptrs, _dtype_code(dts.pop()),
                                            _stream_handle(stream)))
 
-    def step(self, replica_grads: Sequence[Sequence[torch.Tensor]], t: int,
-             params_out: Sequence[torch.Tensor], stream=None):
-        """replica_grads[q][k]: replica q's full gradient of parameter k;
-        params_out[k]: this rank's local shard of parameter k (written)."""
+    def _fsdp_args(self, replica_grads, params_out):
         if len(replica_grads) != self.world:
             raise ValueError(f"need {self.world} replicas, got {len(replica_grads)}")
         gdts = set()
@@ -408,8 +463,22 @@ class FsdpShardState(ShardState):
                             for gl in replica_grads for g in gl])
         optrs = _ptr_array([o.data_ptr() if (o is not None and self.local[k][1]) else 0
                             for k, o in enumerate(params_out)])
-        _check(lib().zero_fsdp_step(self._h, gptrs, self.world, _dtype_code(gdts.pop()), optrs,
+        return gptrs, gdts.pop(), optrs, pdt
+
+    def step(self, replica_grads: Sequence[Sequence[torch.Tensor]], t: int,
+             params_out: Sequence[torch.Tensor], stream=None):
+        """replica_grads[q][k]: replica q's full gradient of parameter k;
+        params_out[k]: this rank's local shard of parameter k (written)."""
+        gptrs, gdt, optrs, pdt = self._fsdp_args(replica_grads, params_out)
+        _check(lib().zero_fsdp_step(self._h, gptrs, self.world, _dtype_code(gdt), optrs,
                                     _dtype_code(pdt), int(t), _stream_handle(stream)))
+
+    def step_sched(self, replica_grads: Sequence[Sequence[torch.Tensor]],
+                   params_out: Sequence[torch.Tensor], stream=None):
+        """step() at the device schedule's next step count and lr."""
+        gptrs, gdt, optrs, pdt = self._fsdp_args(replica_grads, params_out)
+        _check(lib().zero_fsdp_step_sched(self._h, gptrs, self.world, _dtype_code(gdt), optrs,
+                                          _dtype_code(pdt), _stream_handle(stream)))
 
     def state_pieces(self, state: Sequence[torch.Tensor]):
         """Split (master, m, v) from get_state into per-parameter local pieces."""

@@ -31,6 +31,13 @@ struct zero_ctx {
     int num_cus;
     void *state;                 // one allocation: master | m | v
     float *master, *m, *v;
+    // device-resident step schedule (zero_schedule_init), one allocation:
+    // schedule | scalars of the current step | bias-correction table
+    void *sched_mem;
+    zk::DevSchedule *ds;
+    zk::StepScalars *sc_dev;
+    float *bc_table;             // (1-b1^t, 1-b2^t) for t = 1..bc_len
+    int64_t bc_len;
 };
 
 namespace {
@@ -101,11 +108,33 @@ class DeviceGuard {
     hipError_t err_ = hipSuccess;
 };
 
+// Range checks query the runtime's allocation table, which a stream
+// capture in global mode may not allow. While the caller's stream is being
+// captured they are skipped (every other argument check still runs); the
+// buffers of a captured call are normally those of an earlier eager call.
+thread_local bool g_skip_range = false;
+
+class CaptureScope {
+  public:
+    explicit CaptureScope(hipStream_t s) : prev_(g_skip_range) {
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+            (void)hipGetLastError();
+            st = hipStreamCaptureStatusNone;
+        }
+        g_skip_range = st == hipStreamCaptureStatusActive;
+    }
+    ~CaptureScope() { g_skip_range = prev_; }
+
+  private:
+    bool prev_;
+};
+
 // Reject a device range that runs past the allocation holding its first
 // byte (an undersized buffer would otherwise fault on the GPU). Memory the
 // runtime cannot describe (e.g. imported or virtually mapped) is accepted.
 int check_range(const void *p, int64_t nbytes, const char *what) {
-    if (nbytes <= 0) return ZERO_OK;
+    if (nbytes <= 0 || g_skip_range) return ZERO_OK;
     hipDeviceptr_t base = nullptr;
     size_t size = 0;
     hipError_t e = hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)p);
@@ -134,6 +163,24 @@ zk::StepScalars make_scalars(const zero_ctx *c, int64_t t) {
     sc.n_pow2 = (c->world & (c->world - 1)) == 0;
     sc.inv_n = (float)(1.0 / (double)c->world);
     return sc;
+}
+
+// Where a step takes its scalars from.
+enum StepMode {
+    kHostT = 0,          // the step count passed by the caller
+    kBeginDevice = 1,    // begin the schedule's next step, then use its scalars
+    kCurrentDevice = 2,  // the scalars of the schedule's current step
+};
+
+int need_schedule(const zero_ctx *c) {
+    if (!c->sched_mem)
+        return fail(ZERO_EINVAL, "no device step schedule: call zero_schedule_init first");
+    return ZERO_OK;
+}
+
+hipError_t begin_device_step(const zero_ctx *c, hipStream_t stream) {
+    return zk::launch_begin_step(c->ds, c->bc_table, c->bc_len, make_scalars(c, 1), c->sc_dev,
+                                 stream);
 }
 
 int build_flat_segments(const zero_ctx *c, const void *const *tensors, const int64_t *numels,
@@ -364,6 +411,7 @@ int zero_fsdp_load_master(zero_ctx *c, const void *const *params, zero_dtype dty
                           hipStream_t stream) {
     if (!c || !c->fsdp) return fail(ZERO_EINVAL, "not a per-parameter layout context");
     if (!params) return fail(ZERO_EINVAL, "null parameter array");
+    CaptureScope cs(stream);
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dtype);
     const int64_t es = (int64_t)dtype_size(dtype);
     for (size_t k = 0; k < c->tensors.size(); ++k) {
@@ -388,13 +436,20 @@ int zero_fsdp_load_master(zero_ctx *c, const void *const *params, zero_dtype dty
     return ZERO_OK;
 }
 
-int zero_fsdp_step(zero_ctx *c, const void *const *grads, int32_t n_replicas,
-                   zero_dtype grad_dtype, void *const *params_out, zero_dtype param_dtype,
-                   int64_t t, hipStream_t stream) {
+static int fsdp_step_common(zero_ctx *c, const void *const *grads, int32_t n_replicas,
+                            zero_dtype grad_dtype, void *const *params_out,
+                            zero_dtype param_dtype, int64_t t, StepMode mode,
+                            hipStream_t stream) {
     if (!c || !c->fsdp) return fail(ZERO_EINVAL, "not a per-parameter layout context");
+    CaptureScope cs(stream);
     if (n_replicas != c->world)
         return fail(ZERO_EINVAL, "n_replicas (%d) must equal world (%d)", n_replicas, c->world);
-    if (t < 1) return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
+    if (mode == kHostT && t < 1)
+        return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
+    if (mode != kHostT) {
+        int rc = need_schedule(c);
+        if (rc) return rc;
+    }
     if (!grads || !params_out) return fail(ZERO_EINVAL, "null gradient or output array");
     if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
         return fail(ZERO_EINVAL, "unknown dtype");
@@ -430,9 +485,13 @@ int zero_fsdp_step(zero_ctx *c, const void *const *grads, int32_t n_replicas,
         sg.numel = local;
         segs.push_back(sg);
     }
-    if (segs.empty()) return ZERO_OK;
     DeviceGuard g(c->device);
     if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    if (mode == kBeginDevice) {
+        hipError_t e = begin_device_step(c, stream);
+        if (e != hipSuccess) return hip_fail(e, "begin-step launch");
+    }
+    if (segs.empty()) return ZERO_OK;
     zk::FsdpArgs a;
     a.segs = segs.data();
     a.nseg = (int)segs.size();
@@ -442,9 +501,24 @@ int zero_fsdp_step(zero_ctx *c, const void *const *grads, int32_t n_replicas,
     a.master = c->master;
     a.m = c->m;
     a.v = c->v;
-    a.sc = make_scalars(c, t);
+    a.sc = make_scalars(c, mode == kHostT ? t : 1);
+    a.sc_dev = mode == kHostT ? nullptr : c->sc_dev;
     hipError_t e = zk::launch_fsdp_step(a, stream);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "per-parameter step launch");
+}
+
+int zero_fsdp_step(zero_ctx *c, const void *const *grads, int32_t n_replicas,
+                   zero_dtype grad_dtype, void *const *params_out, zero_dtype param_dtype,
+                   int64_t t, hipStream_t stream) {
+    return fsdp_step_common(c, grads, n_replicas, grad_dtype, params_out, param_dtype, t, kHostT,
+                            stream);
+}
+
+int zero_fsdp_step_sched(zero_ctx *c, const void *const *grads, int32_t n_replicas,
+                         zero_dtype grad_dtype, void *const *params_out, zero_dtype param_dtype,
+                         hipStream_t stream) {
+    return fsdp_step_common(c, grads, n_replicas, grad_dtype, params_out, param_dtype, 0,
+                            kBeginDevice, stream);
 }
 
 int zero_shard_info(const zero_ctx *c, int64_t *shard, int64_t *lo, int64_t *padded) {
@@ -466,6 +540,7 @@ int zero_load_master(zero_ctx *c, const void *flat, zero_dtype dtype, int64_t fl
                      hipStream_t stream) {
     if (!c) return fail(ZERO_EINVAL, "null context");
     if (!flat) return fail(ZERO_EINVAL, "null flat parameter buffer");
+    CaptureScope cs(stream);
     if (!valid_dtype(dtype)) return fail(ZERO_EINVAL, "unknown dtype %d", (int)dtype);
     if (flat_offset < 0) return fail(ZERO_EINVAL, "negative offset");
     const size_t es = dtype_size(dtype);
@@ -484,6 +559,8 @@ int zero_load_master(zero_ctx *c, const void *flat, zero_dtype dtype, int64_t fl
 
 int zero_flatten(const zero_ctx *c, const void *const *srcs, const int64_t *numels,
                  int32_t ntensors, zero_dtype dtype, void *dst, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    CaptureScope cs(stream);
     std::vector<zk::Segment> segs;
     int rc = build_flat_segments(c, srcs, numels, ntensors, dtype, dst, segs, true);
     if (rc) return rc;
@@ -497,6 +574,8 @@ int zero_flatten(const zero_ctx *c, const void *const *srcs, const int64_t *nume
 int zero_flatten_range(const zero_ctx *c, const void *const *srcs, const int64_t *numels,
                        int32_t ntensors, zero_dtype dtype, void *dst, int64_t flat_begin,
                        int64_t flat_count, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    CaptureScope cs(stream);
     std::vector<zk::Segment> segs;
     int rc = build_flat_segments(c, srcs, numels, ntensors, dtype, dst, segs, true);
     if (rc) return rc;
@@ -529,6 +608,8 @@ int zero_flatten_range(const zero_ctx *c, const void *const *srcs, const int64_t
 
 int zero_unflatten(const zero_ctx *c, const void *flat, int32_t ntensors, const int64_t *numels,
                    zero_dtype dtype, void *const *dsts, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    CaptureScope cs(stream);
     std::vector<zk::Segment> segs;
     int rc = build_flat_segments(c, (const void *const *)dsts, numels, ntensors, dtype, flat,
                                  segs, false);
@@ -543,15 +624,21 @@ int zero_unflatten(const zero_ctx *c, const void *flat, int32_t ntensors, const 
 static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *const *grads,
                        int32_t n_replicas, zero_dtype grad_dtype, int64_t grad_offset,
                        void *param_out, zero_dtype param_dtype, int64_t param_offset, int64_t t,
-                       hipStream_t stream) {
+                       StepMode mode, hipStream_t stream) {
     if (!c) return fail(ZERO_EINVAL, "null context");
+    CaptureScope cs(stream);
     if (c->fsdp) return reject_fsdp(c);
     if (begin < 0 || count < 0 || begin > c->shard - count)
         return fail(ZERO_EINVAL, "range [%lld, %lld) outside the shard of %lld elements",
                     (long long)begin, (long long)(begin + count), (long long)c->shard);
     if (n_replicas != c->world)
         return fail(ZERO_EINVAL, "n_replicas (%d) must equal world (%d)", n_replicas, c->world);
-    if (t < 1) return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
+    if (mode == kHostT && t < 1)
+        return fail(ZERO_EINVAL, "step t must be >= 1 (got %lld)", (long long)t);
+    if (mode != kHostT) {
+        int rc = need_schedule(c);
+        if (rc) return rc;
+    }
     if (!grads) return fail(ZERO_EINVAL, "null replica array");
     if (!param_out) return fail(ZERO_EINVAL, "null parameter output");
     if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
@@ -569,9 +656,13 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
     if ((uintptr_t)param_out % pe) return fail(ZERO_EINVAL, "parameter output misaligned");
     int rc = check_range(param_out, (param_offset + count) * (int64_t)pe, "parameter output");
     if (rc) return rc;
-    if (count == 0) return ZERO_OK;
     DeviceGuard g(c->device);
     if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    if (mode == kBeginDevice) {
+        hipError_t e = begin_device_step(c, stream);
+        if (e != hipSuccess) return hip_fail(e, "begin-step launch");
+    }
+    if (count == 0) return ZERO_OK;
 
     zk::StepArgs a;
     a.grads = slices;
@@ -583,7 +674,8 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
     a.out = (char *)param_out + (size_t)param_offset * pe;
     a.out_bf16 = param_dtype == ZERO_BF16;
     a.shard = count;
-    a.sc = make_scalars(c, t);
+    a.sc = make_scalars(c, mode == kHostT ? t : 1);
+    a.sc_dev = mode == kHostT ? nullptr : c->sc_dev;
     a.num_cus = c->num_cus;
     hipError_t e = zk::launch_step(a, stream);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "step launch");
@@ -594,7 +686,7 @@ int zero_step(zero_ctx *c, const void *const *grads, int32_t n_replicas, zero_dt
               int64_t t, hipStream_t stream) {
     if (!c) return fail(ZERO_EINVAL, "null context");
     return step_common(c, 0, c->shard, grads, n_replicas, grad_dtype, grad_offset, param_out,
-                       param_dtype, param_offset, t, stream);
+                       param_dtype, param_offset, t, kHostT, stream);
 }
 
 int zero_step_range(zero_ctx *c, int64_t shard_begin, int64_t count, const void *const *grads,
@@ -602,11 +694,126 @@ int zero_step_range(zero_ctx *c, int64_t shard_begin, int64_t count, const void 
                     void *param_out, zero_dtype param_dtype, int64_t param_offset, int64_t t,
                     hipStream_t stream) {
     return step_common(c, shard_begin, count, grads, n_replicas, grad_dtype, grad_offset,
-                       param_out, param_dtype, param_offset, t, stream);
+                       param_out, param_dtype, param_offset, t, kHostT, stream);
+}
+
+int zero_step_sched(zero_ctx *c, const void *const *grads, int32_t n_replicas,
+                    zero_dtype grad_dtype, int64_t grad_offset, void *param_out,
+                    zero_dtype param_dtype, int64_t param_offset, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    return step_common(c, 0, c->shard, grads, n_replicas, grad_dtype, grad_offset, param_out,
+                       param_dtype, param_offset, 0, kBeginDevice, stream);
+}
+
+int zero_step_range_sched(zero_ctx *c, int64_t shard_begin, int64_t count,
+                          const void *const *grads, int32_t n_replicas, zero_dtype grad_dtype,
+                          int64_t grad_offset, void *param_out, zero_dtype param_dtype,
+                          int64_t param_offset, hipStream_t stream) {
+    return step_common(c, shard_begin, count, grads, n_replicas, grad_dtype, grad_offset,
+                       param_out, param_dtype, param_offset, 0, kCurrentDevice, stream);
+}
+
+int zero_step_begin(zero_ctx *c, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    int rc = need_schedule(c);
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    hipError_t e = begin_device_step(c, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "begin-step launch");
+}
+
+// Bias-correction table: entry t-1 holds (f32(1 - b1^t), f32(1 - b2^t)),
+// formed exactly as for a host step count. It ends at the first t where
+// both b^t < 2^-26: from there on 1 - b^t rounds to 1 in binary32 for every
+// later t, and the last entry is (1, 1).
+static int bias_table(const zero_ctx *c, std::vector<float> &tab) {
+    const double tiny = std::ldexp(1.0, -26);
+    int64_t len = 1;
+    while (std::pow(c->beta1, (double)len) >= tiny || std::pow(c->beta2, (double)len) >= tiny) {
+        if (++len > ZERO_SCHEDULE_MAX_TABLE)
+            return fail(ZERO_EUNSUPPORTED, "betas (%g, %g) need a bias-correction table of more "
+                        "than %d steps", c->beta1, c->beta2, ZERO_SCHEDULE_MAX_TABLE);
+    }
+    try {
+        tab.resize((size_t)(2 * len));
+    } catch (...) {
+        return fail(ZERO_ENOMEM, "host allocation failed");
+    }
+    for (int64_t t = 1; t <= len; ++t) {
+        const zk::StepScalars sc = make_scalars(c, t);
+        tab[(size_t)(2 * (t - 1))] = sc.bc1;
+        tab[(size_t)(2 * (t - 1) + 1)] = sc.bc2;
+    }
+    if (tab[(size_t)(2 * len - 2)] != 1.0f || tab[(size_t)(2 * len - 1)] != 1.0f)
+        return fail(ZERO_EHIP, "bias-correction table does not end at (1, 1)");
+    return ZERO_OK;
+}
+
+int zero_schedule_init(zero_ctx *c, int64_t next_t, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (next_t < 1) return fail(ZERO_EINVAL, "next step must be >= 1 (got %lld)", (long long)next_t);
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    if (!c->sched_mem) {
+        std::vector<float> tab;
+        int rc = bias_table(c, tab);
+        if (rc) return rc;
+        const size_t head = 512, bytes = head + tab.size() * sizeof(float);
+        void *mem = nullptr;
+        hipError_t e = hipMalloc(&mem, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(ZERO_ENOMEM, "hipMalloc of %zu bytes for the step schedule failed", bytes);
+        }
+        e = hipMemset(mem, 0, head);
+        if (e == hipSuccess)
+            e = hipMemcpy((char *)mem + head, tab.data(), tab.size() * sizeof(float),
+                          hipMemcpyHostToDevice);
+        if (e != hipSuccess) {
+            (void)hipFree(mem);
+            return hip_fail(e, "uploading the step schedule");
+        }
+        c->sched_mem = mem;
+        c->ds = (zk::DevSchedule *)mem;
+        c->sc_dev = (zk::StepScalars *)((char *)mem + 256);
+        c->bc_table = (float *)((char *)mem + head);
+        c->bc_len = (int64_t)(tab.size() / 2);
+    }
+    hipError_t e = zk::launch_set_schedule(c->ds, next_t, (float)c->lr, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "schedule launch");
+}
+
+int zero_schedule_lr(zero_ctx *c, double lr, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (!std::isfinite(lr)) return fail(ZERO_EINVAL, "lr must be finite");
+    int rc = need_schedule(c);
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    c->lr = lr;
+    hipError_t e = zk::launch_set_schedule(c->ds, 0, (float)lr, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "schedule launch");
+}
+
+int zero_schedule_get(const zero_ctx *c, int64_t *next_t, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (!next_t) return fail(ZERO_EINVAL, "null output pointer");
+    int rc = need_schedule(c);
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    zk::DevSchedule h;
+    hipError_t e = hipMemcpyAsync(&h, c->ds, sizeof h, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "reading the step schedule");
+    *next_t = h.t;
+    return ZERO_OK;
 }
 
 static int copy_state(const zero_ctx *c, const float *const src[3], float *const dst[3],
                       hipStream_t stream, const char *what) {
+    CaptureScope cs(stream);
     DeviceGuard g(c->device);
     if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
     for (int k = 0; k < 3; ++k) {
@@ -641,6 +848,7 @@ void zero_destroy(zero_ctx *c) {
     DeviceGuard g(c->device);
     (void)hipDeviceSynchronize();
     if (c->state) (void)hipFree(c->state);
+    if (c->sched_mem) (void)hipFree(c->sched_mem);
     delete c;
 }
 

@@ -18,8 +18,18 @@ struct StepScalars {
     int n_pow2;
 };
 
+// Device-resident step schedule (graph-replayable steps): the step count
+// of the next step and the fp32 learning rate, in device memory.
+struct DevSchedule {
+    int64_t t;
+    float lr;
+    int32_t pad;
+};
+
 // One step over `shard` elements. grads[q] already points at element 0 of
-// replica q's slice; out at element 0 of the output slice.
+// replica q's slice; out at element 0 of the output slice. With sc_dev
+// non-null the kernels read their scalars from that device address
+// (written by launch_begin_step) and `sc` is unused.
 struct StepArgs {
     const void *const *grads;   // host array, n entries
     int n;
@@ -29,9 +39,19 @@ struct StepArgs {
     bool out_bf16;
     int64_t shard;
     StepScalars sc;
+    const StepScalars *sc_dev;
     int num_cus;
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t stream);
+
+// Resolve the scalars of the schedule's current step into *out: `base`
+// supplies the step-independent ones, ds->lr the learning rate, and
+// table[min(t, len) - 1] the bias corrections (1-b1^t, 1-b2^t); then
+// advance ds->t by one. One lane of one workgroup.
+hipError_t launch_begin_step(DevSchedule *ds, const float *table, int64_t len,
+                             const StepScalars &base, StepScalars *out, hipStream_t stream);
+// ds->t = t (if t >= 1) and ds->lr = lr, stream-ordered.
+hipError_t launch_set_schedule(DevSchedule *ds, int64_t t, float lr, hipStream_t stream);
 
 // Per-parameter (dim-0) layout: one segment per parameter's local shard.
 constexpr int kFsdpMaxWorld = 16;
@@ -48,6 +68,7 @@ struct FsdpArgs {
     bool grad_bf16, out_bf16;
     float *master, *m, *v;
     StepScalars sc;
+    const StepScalars *sc_dev;    // as in StepArgs
 };
 hipError_t launch_fsdp_step(const FsdpArgs &a, hipStream_t stream);
 

@@ -142,6 +142,16 @@ struct Reps {
     const void *p[NR > 0 ? NR : ZERO_MAX_WORLD];
 };
 
+// Where a step kernel takes its scalars from: by value in the kernel
+// arguments, or (DS) from device memory written by the begin-step kernel,
+// which lets a captured graph replay successive steps.
+template <bool DS> struct ScalarArg;
+template <> struct ScalarArg<false> { StepScalars v; };
+template <> struct ScalarArg<true> { const StepScalars *p; };
+
+__device__ __forceinline__ StepScalars scalars(const ScalarArg<false> &a) { return a.v; }
+__device__ __forceinline__ StepScalars scalars(const ScalarArg<true> &a) { return *a.p; }
+
 // Raw 8-element gradient vector of one replica: 16 bytes of bf16 or 32
 // bytes of fp32.
 template <bool GB> struct RawVec;
@@ -268,11 +278,12 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
 // [8j, 8j+8) of vector j. NR > 0 fixes the replica count at compile time
 // (N <= 16 fully unrolled; larger N walks the groups in a loop to bound
 // register use); NR == 0 reads it from `nrep`.
-template <int NR, bool GB, bool PB>
+template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
                 float *__restrict__ mom, float *__restrict__ var,
-                void *__restrict__ out, int64_t nvec, StepScalars sc) {
+                void *__restrict__ out, int64_t nvec, ScalarArg<DS> sa) {
+    const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
@@ -306,12 +317,13 @@ __device__ __forceinline__ void step_one(const Reps<NR> &reps, int n, float *__r
 
 // Element path: any alignment, and the tail of the vector path. Lane
 // handles element i, consecutive lanes consecutive elements.
-template <bool GB, bool PB>
+template <bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kElemBlock)
 step_elem_kernel(Reps<0> reps, int nrep, float *__restrict__ master,
                  float *__restrict__ mom, float *__restrict__ var,
                  void *__restrict__ out, int64_t begin, int64_t end,
-                 StepScalars sc) {
+                 ScalarArg<DS> sa) {
+    const StepScalars sc = scalars(sa);
     const int64_t stride = (int64_t)gridDim.x * kElemBlock;
     for (int64_t i = begin + (int64_t)blockIdx.x * kElemBlock + threadIdx.x; i < end; i += stride)
         step_one<0, GB, PB>(reps, nrep, master, mom, var, out, i, sc);
@@ -517,11 +529,12 @@ __device__ __forceinline__ void store_f32x8_at(float *q, int d, const float (&x)
 // Vector j of the shifted path: state aligned; replicas read through
 // their aligned bases; the output (element pointer of the range's first
 // element, dout elements past a 16-byte boundary) written at its phase.
-template <int NR, bool GB, bool PB>
+template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
                   float *__restrict__ mom, float *__restrict__ var, void *__restrict__ out,
-                  int dout, int64_t nvec, StepScalars sc) {
+                  int dout, int64_t nvec, ScalarArg<DS> sa) {
+    const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
@@ -588,10 +601,11 @@ struct FsdpBatch {
     int nseg;
 };
 
-template <int NR, bool EXACT, bool GB, bool PB>
+template <int NR, bool EXACT, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 fsdp_step_kernel(FsdpBatch<NR> b, int nrep, float *__restrict__ master,
-                 float *__restrict__ mom, float *__restrict__ var, StepScalars sc) {
+                 float *__restrict__ mom, float *__restrict__ var, ScalarArg<DS> sa) {
+    const StepScalars sc = scalars(sa);
     const int64_t w = blockIdx.x;
     int lo = 0, hi = b.nseg - 1;                 // last segment with blk0 <= w
     while (lo < hi) {
@@ -621,7 +635,18 @@ fsdp_step_kernel(FsdpBatch<NR> b, int nrep, float *__restrict__ master,
     }
 }
 
-template <int NR, bool EXACT, bool GB, bool PB>
+template <bool DS>
+ScalarArg<DS> scalar_arg(const StepScalars &sc, const StepScalars *dev);
+template <>
+inline ScalarArg<false> scalar_arg<false>(const StepScalars &sc, const StepScalars *) {
+    return ScalarArg<false>{sc};
+}
+template <>
+inline ScalarArg<true> scalar_arg<true>(const StepScalars &, const StepScalars *dev) {
+    return ScalarArg<true>{dev};
+}
+
+template <int NR, bool EXACT, bool GB, bool PB, bool DS>
 hipError_t launch_fsdp_typed(const FsdpArgs &a, hipStream_t stream) {
     const int64_t per_block = (int64_t)kBlock * kVec;
     int i = 0;
@@ -643,51 +668,53 @@ hipError_t launch_fsdp_typed(const FsdpArgs &a, hipStream_t stream) {
         if (b.nseg == 0) continue;
         b.blk0[b.nseg] = blocks;
         if (blocks > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((fsdp_step_kernel<NR, EXACT, GB, PB>), dim3((unsigned)blocks),
-                           dim3(kBlock), ZK_STEP_LDS, stream, b, a.n, a.master, a.m, a.v, a.sc);
+        hipLaunchKernelGGL((fsdp_step_kernel<NR, EXACT, GB, PB, DS>), dim3((unsigned)blocks),
+                           dim3(kBlock), ZK_STEP_LDS, stream, b, a.n, a.master, a.m, a.v,
+                           scalar_arg<DS>(a.sc, a.sc_dev));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
-template <bool GB, bool PB>
+template <bool GB, bool PB, bool DS>
 hipError_t launch_fsdp_dtype(const FsdpArgs &a, hipStream_t stream) {
     switch (a.n) {
-    case 1: return launch_fsdp_typed<1, true, GB, PB>(a, stream);
-    case 2: return launch_fsdp_typed<2, true, GB, PB>(a, stream);
-    case 4: return launch_fsdp_typed<4, true, GB, PB>(a, stream);
-    case 8: return launch_fsdp_typed<8, true, GB, PB>(a, stream);
-    default: return launch_fsdp_typed<kFsdpMaxWorld, false, GB, PB>(a, stream);
+    case 1: return launch_fsdp_typed<1, true, GB, PB, DS>(a, stream);
+    case 2: return launch_fsdp_typed<2, true, GB, PB, DS>(a, stream);
+    case 4: return launch_fsdp_typed<4, true, GB, PB, DS>(a, stream);
+    case 8: return launch_fsdp_typed<8, true, GB, PB, DS>(a, stream);
+    default: return launch_fsdp_typed<kFsdpMaxWorld, false, GB, PB, DS>(a, stream);
     }
 }
 
-template <int NR, bool GB, bool PB>
+template <int NR, bool GB, bool PB, bool DS>
 hipError_t launch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
     Reps<NR> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
     const int64_t grid = (nvec + kBlock - 1) / kBlock;
     // a dispatch holds at most 2^32-1 work-items
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB>), dim3((unsigned)grid), dim3(kBlock),
-                       ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, a.sc);
+    hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
+                       ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec,
+                       scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
-template <bool GB, bool PB>
+template <bool GB, bool PB, bool DS>
 hipError_t dispatch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
     switch (a.n) {
-    case 1: return launch_vec<1, GB, PB>(a, nvec, stream);
-    case 2: return launch_vec<2, GB, PB>(a, nvec, stream);
-    case 4: return launch_vec<4, GB, PB>(a, nvec, stream);
-    case 8: return launch_vec<8, GB, PB>(a, nvec, stream);
-    case 16: return launch_vec<16, GB, PB>(a, nvec, stream);
-    case 64: return launch_vec<64, GB, PB>(a, nvec, stream);
-    default: return launch_vec<0, GB, PB>(a, nvec, stream);
+    case 1: return launch_vec<1, GB, PB, DS>(a, nvec, stream);
+    case 2: return launch_vec<2, GB, PB, DS>(a, nvec, stream);
+    case 4: return launch_vec<4, GB, PB, DS>(a, nvec, stream);
+    case 8: return launch_vec<8, GB, PB, DS>(a, nvec, stream);
+    case 16: return launch_vec<16, GB, PB, DS>(a, nvec, stream);
+    case 64: return launch_vec<64, GB, PB, DS>(a, nvec, stream);
+    default: return launch_vec<0, GB, PB, DS>(a, nvec, stream);
     }
 }
 
-template <bool GB, bool PB>
+template <bool GB, bool PB, bool DS>
 hipError_t launch_elem(const StepArgs &a, int64_t begin, int64_t end, hipStream_t stream) {
     Reps<0> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
@@ -695,8 +722,9 @@ hipError_t launch_elem(const StepArgs &a, int64_t begin, int64_t end, hipStream_
     int64_t cap = (int64_t)a.num_cus * 8;
     int grid = (int)(want < cap ? want : cap);
     if (grid < 1) grid = 1;
-    hipLaunchKernelGGL((step_elem_kernel<GB, PB>), dim3(grid), dim3(kElemBlock), 0, stream,
-                       reps, a.n, a.master, a.m, a.v, a.out, begin, end, a.sc);
+    hipLaunchKernelGGL((step_elem_kernel<GB, PB, DS>), dim3(grid), dim3(kElemBlock), 0, stream,
+                       reps, a.n, a.master, a.m, a.v, a.out, begin, end,
+                       scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
@@ -737,7 +765,7 @@ inline int shifted_head(const StepArgs &a) {
     return best;
 }
 
-template <int NR, bool GB, bool PB>
+template <int NR, bool GB, bool PB, bool DS>
 hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stream) {
     const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
     ShiftReps<NR> reps;
@@ -750,41 +778,41 @@ hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stre
     const int dout = (int)(((uintptr_t)out % 16) / oe);
     const int64_t grid = (nvec + kBlock - 1) / kBlock;
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((step_shift_kernel<NR, GB, PB>), dim3((unsigned)grid), dim3(kBlock),
+    hipLaunchKernelGGL((step_shift_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
                        ZK_STEP_LDS, stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
-                       nvec, a.sc);
+                       nvec, scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
-template <bool GB, bool PB>
+template <bool GB, bool PB, bool DS>
 hipError_t dispatch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stream) {
     switch (a.n) {
-    case 1: return launch_shift<1, GB, PB>(a, h, nvec, stream);
-    case 2: return launch_shift<2, GB, PB>(a, h, nvec, stream);
-    case 4: return launch_shift<4, GB, PB>(a, h, nvec, stream);
-    case 8: return launch_shift<8, GB, PB>(a, h, nvec, stream);
-    case 16: return launch_shift<16, GB, PB>(a, h, nvec, stream);
-    case 64: return launch_shift<64, GB, PB>(a, h, nvec, stream);
-    default: return launch_shift<0, GB, PB>(a, h, nvec, stream);
+    case 1: return launch_shift<1, GB, PB, DS>(a, h, nvec, stream);
+    case 2: return launch_shift<2, GB, PB, DS>(a, h, nvec, stream);
+    case 4: return launch_shift<4, GB, PB, DS>(a, h, nvec, stream);
+    case 8: return launch_shift<8, GB, PB, DS>(a, h, nvec, stream);
+    case 16: return launch_shift<16, GB, PB, DS>(a, h, nvec, stream);
+    case 64: return launch_shift<64, GB, PB, DS>(a, h, nvec, stream);
+    default: return launch_shift<0, GB, PB, DS>(a, h, nvec, stream);
     }
 }
 
 // Element head [0, h), vector range, element tail.
-template <bool GB, bool PB>
+template <bool GB, bool PB, bool DS>
 hipError_t step_shifted(const StepArgs &a, int h, hipStream_t stream) {
     const int64_t nvec = (a.shard - h) / kVec;
     if (h > 0) {
-        hipError_t e = launch_elem<GB, PB>(a, 0, h, stream);
+        hipError_t e = launch_elem<GB, PB, DS>(a, 0, h, stream);
         if (e != hipSuccess) return e;
     }
-    hipError_t e = dispatch_shift<GB, PB>(a, h, nvec, stream);
+    hipError_t e = dispatch_shift<GB, PB, DS>(a, h, nvec, stream);
     if (e != hipSuccess) return e;
     const int64_t done = h + nvec * kVec;
-    if (done < a.shard) return launch_elem<GB, PB>(a, done, a.shard, stream);
+    if (done < a.shard) return launch_elem<GB, PB, DS>(a, done, a.shard, stream);
     return hipSuccess;
 }
 
-template <bool GB, bool PB>
+template <bool GB, bool PB, bool DS>
 hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     // Vector path from the first element at which all streams are 16-byte
     // aligned; the few elements before it and the ragged tail take the
@@ -795,13 +823,13 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     const int h = common_head(a);
     if (h < 0) {
         const int hs = shifted_head(a);
-        if (hs >= 0 && a.shard - hs >= kVec) return step_shifted<GB, PB>(a, hs, stream);
-        return launch_elem<GB, PB>(a, 0, a.shard, stream);
+        if (hs >= 0 && a.shard - hs >= kVec) return step_shifted<GB, PB, DS>(a, hs, stream);
+        return launch_elem<GB, PB, DS>(a, 0, a.shard, stream);
     }
-    if (a.shard - h < kVec) return launch_elem<GB, PB>(a, 0, a.shard, stream);
+    if (a.shard - h < kVec) return launch_elem<GB, PB, DS>(a, 0, a.shard, stream);
     const int64_t nvec = (a.shard - h) / kVec;
     if (h > 0) {
-        hipError_t e = launch_elem<GB, PB>(a, 0, h, stream);
+        hipError_t e = launch_elem<GB, PB, DS>(a, 0, h, stream);
         if (e != hipSuccess) return e;
     }
     StepArgs b = a;
@@ -813,10 +841,10 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     b.m = a.m + h;
     b.v = a.v + h;
     b.out = (char *)a.out + (int64_t)oe * h;
-    hipError_t e = dispatch_vec<GB, PB>(b, nvec, stream);
+    hipError_t e = dispatch_vec<GB, PB, DS>(b, nvec, stream);
     if (e != hipSuccess) return e;
     const int64_t done = h + nvec * kVec;
-    if (done < a.shard) return launch_elem<GB, PB>(a, done, a.shard, stream);
+    if (done < a.shard) return launch_elem<GB, PB, DS>(a, done, a.shard, stream);
     return hipSuccess;
 }
 
@@ -903,24 +931,77 @@ load_master_kernel(const void *__restrict__ flat, float *__restrict__ master,
     }
 }
 
+// ------------------------------------------------------ device step schedule
+// One lane: the scalars of the schedule's current step, then t advances.
+// Bias corrections come from the host-built table (binary64 power, one
+// rounding to binary32); past its end both are exactly 1.
+__global__ void __launch_bounds__(64)
+begin_step_kernel(DevSchedule *ds, const float *__restrict__ table, int64_t len,
+                  StepScalars base, StepScalars *out) {
+    if (threadIdx.x != 0) return;
+    const int64_t t = ds->t;
+    int64_t i = t < 1 ? 1 : t;
+    if (i > len) i = len;
+    StepScalars sc = base;
+    sc.lr = ds->lr;
+    sc.bc1 = table[2 * (i - 1)];
+    sc.bc2 = table[2 * (i - 1) + 1];
+    *out = sc;
+    ds->t = t + 1;
+}
+
+__global__ void __launch_bounds__(64)
+set_schedule_kernel(DevSchedule *ds, int64_t t, float lr) {
+    if (threadIdx.x != 0) return;
+    if (t >= 1) ds->t = t;
+    ds->lr = lr;
+}
+
 }  // namespace
+
+hipError_t launch_begin_step(DevSchedule *ds, const float *table, int64_t len,
+                             const StepScalars &base, StepScalars *out, hipStream_t stream) {
+    hipLaunchKernelGGL(begin_step_kernel, dim3(1), dim3(64), 0, stream, ds, table, len, base, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_set_schedule(DevSchedule *ds, int64_t t, float lr, hipStream_t stream) {
+    hipLaunchKernelGGL(set_schedule_kernel, dim3(1), dim3(64), 0, stream, ds, t, lr);
+    return hipGetLastError();
+}
 
 hipError_t launch_step(const StepArgs &a, hipStream_t stream) {
     if (a.shard <= 0) return hipSuccess;
-    if (a.grad_bf16) {
-        return a.out_bf16 ? step_typed<true, true>(a, stream) : step_typed<true, false>(a, stream);
+    if (a.sc_dev) {
+        if (a.grad_bf16)
+            return a.out_bf16 ? step_typed<true, true, true>(a, stream)
+                              : step_typed<true, false, true>(a, stream);
+        return a.out_bf16 ? step_typed<false, true, true>(a, stream)
+                          : step_typed<false, false, true>(a, stream);
     }
-    return a.out_bf16 ? step_typed<false, true>(a, stream) : step_typed<false, false>(a, stream);
+    if (a.grad_bf16) {
+        return a.out_bf16 ? step_typed<true, true, false>(a, stream)
+                          : step_typed<true, false, false>(a, stream);
+    }
+    return a.out_bf16 ? step_typed<false, true, false>(a, stream)
+                      : step_typed<false, false, false>(a, stream);
 }
 
 hipError_t launch_fsdp_step(const FsdpArgs &a, hipStream_t stream) {
     if (a.n < 1 || a.n > kFsdpMaxWorld) return hipErrorInvalidValue;
-    if (a.grad_bf16) {
-        return a.out_bf16 ? launch_fsdp_dtype<true, true>(a, stream)
-                          : launch_fsdp_dtype<true, false>(a, stream);
+    if (a.sc_dev) {
+        if (a.grad_bf16)
+            return a.out_bf16 ? launch_fsdp_dtype<true, true, true>(a, stream)
+                              : launch_fsdp_dtype<true, false, true>(a, stream);
+        return a.out_bf16 ? launch_fsdp_dtype<false, true, true>(a, stream)
+                          : launch_fsdp_dtype<false, false, true>(a, stream);
     }
-    return a.out_bf16 ? launch_fsdp_dtype<false, true>(a, stream)
-                      : launch_fsdp_dtype<false, false>(a, stream);
+    if (a.grad_bf16) {
+        return a.out_bf16 ? launch_fsdp_dtype<true, true, false>(a, stream)
+                          : launch_fsdp_dtype<true, false, false>(a, stream);
+    }
+    return a.out_bf16 ? launch_fsdp_dtype<false, true, false>(a, stream)
+                      : launch_fsdp_dtype<false, false, false>(a, stream);
 }
 
 hipError_t launch_copy_segments(const Segment *segs, int nseg, int esize, hipStream_t stream) {
