@@ -120,8 +120,11 @@ def cpu_baseline(window: int, min_seconds: float):
     oracle.set_threads(1)
     iters1, el1 = run(min_seconds / 2)
     oracle.set_threads(threads)
+    # host bytes per iteration with the GPU kernels' formulas: the fused
+    # step's 42 B per shard element plus the flatten's read and write
+    host_bytes = step_bytes_per_elem(WORLD) * window + 2 * 2 * WORLD * window
     return dict(value=window * iters / el, unit="shard elements/s", cores=threads,
-                kind="oracle",
+                kind="oracle", host_gbps=host_bytes * iters / el / 1e9,
                 sample=(f"{iters} steps of a {window}-element window of the 7e9/N=8 shard: "
                         f"flatten of {WORLD * window} bf16 gradient elements + reduce/Adam/bf16 "
                         f"over {WORLD} replicas, {el:.1f} s wall on {threads} OpenMP threads"),
@@ -466,12 +469,14 @@ def main():
         extras["fsdp_llama7b_n8_rank0"] = fsdp_extras(dev)
 
     kernels = {
-        "fused_step": {"ms_mean": float(step_ms.mean()), "ms_min": float(step_ms.min()),
+        "fused_step": {"ms_mean": float(step_ms.mean()), "ms_median": float(np.median(step_ms)),
+                       "ms_min": float(step_ms.min()),
                        "bytes_per_launch": k2_bytes, "bytes_per_elem": bpe,
                        "gbps": k2_gbps, "elements_per_s": S / (step_ms.mean() * 1e-3)},
     }
     if k1_bytes:
-        kernels["flatten"] = {"ms_mean": float(flat_ms.mean()), "ms_min": float(flat_ms.min()),
+        kernels["flatten"] = {"ms_mean": float(flat_ms.mean()), "ms_median": float(np.median(flat_ms)),
+                              "ms_min": float(flat_ms.min()),
                               "bytes_per_launch": k1_bytes, "tensors": ntensors,
                               "gbps": k1_bytes / (flat_ms.mean() * 1e-3) / 1e9}
     result = {
