@@ -283,7 +283,10 @@ int zero_step_sched(zero_ctx *ctx, const void *const *grad_replicas,
 
 /* zero_step_range at the schedule's current step (the one the last
  * zero_step_begin began); covering the shard with disjoint ranges after
- * one zero_step_begin equals one zero_step_sched. */
+ * one zero_step_begin equals one zero_step_sched. The ranges read the
+ * scalars zero_step_begin wrote: a range on another stream must be ordered
+ * after that zero_step_begin (e.g. by an event), and must have finished
+ * before the next zero_step_begin runs. */
 int zero_step_range_sched(zero_ctx *ctx, int64_t shard_begin, int64_t count,
                           const void *const *grad_replicas,
                           int32_t n_replicas, zero_dtype grad_dtype,

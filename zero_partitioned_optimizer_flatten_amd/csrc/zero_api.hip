@@ -50,7 +50,11 @@ int fail(int code, const char *fmt, ...) {
     va_start(ap, fmt);
     vsnprintf(buf, sizeof buf, fmt, ap);
     va_end(ap);
-    g_last_error = buf;
+    try {
+        g_last_error = buf;
+    } catch (...) {
+        g_last_error.clear();
+    }
     return code;
 }
 
@@ -195,7 +199,11 @@ int build_flat_segments(const zero_ctx *c, const void *const *tensors, const int
     const int64_t es = (int64_t)dtype_size(dtype);
     int64_t off = 0;
     segs.clear();
-    segs.reserve((size_t)ntensors + 1);
+    try {
+        segs.reserve((size_t)ntensors + 1);
+    } catch (...) {
+        return fail(ZERO_ENOMEM, "host allocation failed");
+    }
     for (int32_t t = 0; t < ntensors; ++t) {
         const int64_t n = numels[t];
         if (n < 0) return fail(ZERO_EINVAL, "numels[%d] is negative", t);
@@ -588,7 +596,11 @@ int zero_flatten_range(const zero_ctx *c, const void *const *srcs, const int64_t
     const char *base = (const char *)dst;
     const int64_t wb = flat_begin * es, we = (flat_begin + flat_count) * es;
     std::vector<zk::Segment> clipped;
-    clipped.reserve(segs.size());
+    try {
+        clipped.reserve(segs.size());
+    } catch (...) {
+        return fail(ZERO_ENOMEM, "host allocation failed");
+    }
     for (const zk::Segment &sg : segs) {
         const int64_t b = (const char *)sg.dst - base, e = b + sg.nbytes;
         const int64_t cb = b > wb ? b : wb, ce = e < we ? e : we;
