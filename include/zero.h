@@ -247,7 +247,10 @@ int zero_fsdp_step(zero_ctx *ctx, const void *const *grads, int32_t n_replicas,
  * the host at zero_schedule_init exactly as it forms them for a host t.
  * Between zero_schedule_init and zero_destroy the scheduled calls launch
  * kernels only (no allocation, no memset, no host synchronisation), so
- * they can be recorded by HIP stream capture. */
+ * they can be recorded by HIP stream capture. Scheduled calls on one
+ * context must be ordered among themselves (one stream, or events between
+ * streams): every zero_step_begin advances the same device counter and
+ * rewrites the same block of scalars. */
 
 /* Longest bias-correction table (in steps) the schedule accepts; betas for
  * which 1 - b^t has not reached 1 in binary32 by then are EUNSUPPORTED. */
