@@ -199,7 +199,8 @@ int zero_dim0_split(int64_t dim0, int32_t world, int32_t rank,
 /* Context for `ntensors` parameters, parameter k having dim0[k] rows of
  * row_numel[k] elements (row-major). The library allocates fp32 master, m
  * and v for this rank's rows of every parameter, concatenated in order with
- * each piece starting on a multiple of 8 elements, all zero.
+ * each piece starting on a multiple of 32 elements (a 128-byte line), all
+ * zero.
  * zero_shard_info reports the state length as `shard` (lo = 0).
  * zero_get_state / zero_set_state / zero_set_lr / zero_destroy apply;
  * the flat-layout calls (zero_load_master, zero_flatten, zero_unflatten,

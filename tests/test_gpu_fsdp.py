@@ -82,9 +82,11 @@ def test_fsdp_flat_calls_rejected_and_geometry():
     st = zero.FsdpShardState([(10, 3), (5,)], 4, 3, 1e-3)
     assert [st.local[k][:2] for k in range(2)] == [oracle.dim0_split(10, 4, 3),
                                                    oracle.dim0_split(5, 4, 3)]
+    n = st.shard                     # the concatenated local state, in whole lines
+    assert n == 32
     with pytest.raises(zero.ZeroError) as e:
-        zero.ShardState.step(st, [torch.zeros(8, device="cuda")] * 4, 1,
-                             torch.zeros(8, device="cuda"))
+        zero.ShardState.step(st, [torch.zeros(n, device="cuda")] * 4, 1,
+                             torch.zeros(n, device="cuda"))
     assert e.value.code == zero.ZERO_EINVAL
     st.close()
 

@@ -18,7 +18,7 @@
 struct zero_fsdp_tensor {
     int64_t dim0, row_numel;     // full shape: dim0 rows of row_numel elements
     int64_t first_row, rows;     // this rank's rows
-    int64_t state_off;           // first element in master/m/v (multiple of 8)
+    int64_t state_off;           // first element in master/m/v (multiple of 32)
 };
 
 struct zero_ctx {
@@ -269,10 +269,14 @@ static int check_hparams(int32_t world, double lr, double beta1, double beta2, d
 }
 
 // Device, master/m/v (`shard` elements each, zeroed) for a filled-in context.
-// Each array starts `shift` elements past a 256-byte boundary: with shift =
-// lo mod 4, element i of the state and element lo + i of any 16-byte
-// aligned full flat buffer share their offset within 16 bytes, so a step
-// on full flat buffers at an unaligned lo still runs 16-byte vectors.
+// Each array starts `shift` elements past a 256-byte boundary. With shift =
+// lo mod 32 the state lines up with full flat buffers that start on a
+// 128-byte line: at h = (-lo) mod 64, element lo + h of such a buffer is at
+// a multiple of 128 bytes (bf16: 2(lo + h); fp32: 4(lo + h)), and so is
+// state element h (4(shift + h), with shift + h = lo + h mod 32). A step on
+// full flat buffers at any lo therefore runs, after a head of fewer than 64
+// elements, on wavefront blocks that fill whole 128-byte lines of every
+// stream.
 static int alloc_state(zero_ctx *c, int shift) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -327,7 +331,7 @@ int zero_shard_init(int64_t numel, int32_t world, int32_t rank, double lr, doubl
     c->beta1 = beta1;
     c->beta2 = beta2;
     c->eps = eps;
-    rc = alloc_state(c, (int)(lo % 4));
+    rc = alloc_state(c, (int)(lo % 32));
     if (rc) {
         delete c;
         return rc;
@@ -388,7 +392,7 @@ int zero_fsdp_init(int32_t ntensors, const int64_t *dim0, const int64_t *row_num
         t.row_numel = row_numel[k];
         dim0_split(t.dim0, world, rank, &t.first_row, &t.rows);
         t.state_off = off;
-        off += (t.rows * t.row_numel + 7) / 8 * 8;   // keep every shard 32-byte aligned
+        off += (t.rows * t.row_numel + 31) / 32 * 32;   // every piece on a 128-byte line
         total += t.dim0 * t.row_numel;
     }
     c->numel = total;

@@ -728,35 +728,62 @@ hipError_t launch_elem(const StepArgs &a, int64_t begin, int64_t end, hipStream_
     return hipGetLastError();
 }
 
-// Smallest h in [0, 8) at which every stream sits on a 16-byte boundary
-// (element h of a bf16 stream at byte 2h, of an fp32 stream at 4h), or -1.
-inline int common_head(const StepArgs &a) {
+// Cache-line size of the L2: a wavefront's block of a stream (1 KiB of
+// bf16, 2 KiB of fp32) fills whole lines when the vector range starts on a
+// line. Adjacent workgroups run on different XCDs, each with its own L2, so
+// a line shared by two blocks is fetched, or written, twice.
+constexpr uintptr_t kLine = 128;
+constexpr int kLineHead = 64;        // bf16 elements per line: heads below this
+
+inline bool at(const void *p, int esize, int h, uintptr_t align) {
+    return ((uintptr_t)p + (uintptr_t)esize * (uintptr_t)h) % align == 0;
+}
+
+inline bool state_at(const StepArgs &a, int h, uintptr_t align) {
+    return at(a.master, 4, h, align) && at(a.m, 4, h, align) && at(a.v, 4, h, align);
+}
+
+// Every stream (replicas, master/m/v, output) at element h on an `align`
+// boundary (element h of a bf16 stream at byte 2h, of an fp32 stream at 4h).
+inline bool all_at(const StepArgs &a, int h, uintptr_t align) {
     const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
-    for (int h = 0; h < kVec; ++h) {
-        bool ok = ((uintptr_t)a.master + 4u * h) % 16 == 0 && ((uintptr_t)a.m + 4u * h) % 16 == 0 &&
-                  ((uintptr_t)a.v + 4u * h) % 16 == 0 && ((uintptr_t)a.out + (uintptr_t)oe * h) % 16 == 0;
-        for (int q = 0; q < a.n && ok; ++q) ok = ((uintptr_t)a.grads[q] + (uintptr_t)ge * h) % 16 == 0;
-        if (ok) return h;
-    }
+    bool ok = state_at(a, h, align) && at(a.out, oe, h, align);
+    for (int q = 0; q < a.n && ok; ++q) ok = at(a.grads[q], ge, h, align);
+    return ok;
+}
+
+// Head of the vector path: the smallest h < 64 at which every stream sits
+// on a 128-byte line; failing that, the smallest h < 8 at which every
+// stream sits on a 16-byte boundary; -1 if neither exists.
+inline int common_head(const StepArgs &a) {
+    for (int h = 0; h < kLineHead; ++h)
+        if (all_at(a, h, kLine)) return h;
+    for (int h = 0; h < kVec; ++h)
+        if (all_at(a, h, 16)) return h;
     return -1;
 }
 
-// Head for the shifted path: the h in [0, 8) at which master, m and v are
-// 16-byte aligned and the most caller streams are too (the output counts
-// double: its unaligned form costs more instructions than a replica's), or
-// -1 if no h aligns the state or a buffer is not naturally aligned.
+// Head for the shifted path: an h < 64 at which master, m and v are 16-byte
+// aligned, chosen for, in order: the state on a 128-byte line, the most
+// caller streams on a line (the output counts double: its unaligned form
+// also costs more instructions than a replica's), the most on a 16-byte
+// boundary; the smallest such h. -1 if no h aligns the state or a buffer
+// is not naturally aligned.
 inline int shifted_head(const StepArgs &a) {
     const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
     if ((uintptr_t)a.out % oe) return -1;
     for (int q = 0; q < a.n; ++q)
         if ((uintptr_t)a.grads[q] % ge) return -1;
-    int best = -1, best_score = -1;
-    for (int h = 0; h < kVec; ++h) {
-        if (((uintptr_t)a.master + 4u * h) % 16 || ((uintptr_t)a.m + 4u * h) % 16 ||
-            ((uintptr_t)a.v + 4u * h) % 16)
-            continue;
-        int score = ((uintptr_t)a.out + (uintptr_t)oe * h) % 16 == 0 ? 2 : 0;
-        for (int q = 0; q < a.n; ++q) score += ((uintptr_t)a.grads[q] + (uintptr_t)ge * h) % 16 == 0;
+    int best = -1;
+    int64_t best_score = -1;
+    for (int h = 0; h < kLineHead; ++h) {
+        if (!state_at(a, h, 16)) continue;
+        int64_t lines = 2 * at(a.out, oe, h, kLine), vecs = 2 * at(a.out, oe, h, 16);
+        for (int q = 0; q < a.n; ++q) {
+            lines += at(a.grads[q], ge, h, kLine);
+            vecs += at(a.grads[q], ge, h, 16);
+        }
+        const int64_t score = (int64_t)state_at(a, h, kLine) * (1 << 20) + lines * 1024 + vecs;
         if (score > best_score) {
             best = h;
             best_score = score;
