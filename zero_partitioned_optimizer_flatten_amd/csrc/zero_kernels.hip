@@ -274,35 +274,57 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
     }
 }
 
+// One element i of the fused step (any alignment). R is a replica table:
+// rep_base(reps, q, element size) gives replica q's element 0.
+template <int NR, bool GB, bool PB, class R>
+__device__ __forceinline__ void step_one(const R &reps, int n, float *__restrict__ master,
+                                         float *__restrict__ mom, float *__restrict__ var,
+                                         void *__restrict__ out, int64_t i, const StepScalars &sc);
+
+template <int NR>
+__device__ __forceinline__ const void *rep_base(const Reps<NR> &r, int q, int) {
+    return r.p[q];
+}
+
 // Vector path: every stream 16-byte aligned; lane handles elements
 // [8j, 8j+8) of vector j. NR > 0 fixes the replica count at compile time
 // (N <= 16 fully unrolled; larger N walks the groups in a loop to bound
-// register use); NR == 0 reads it from `nrep`.
+// register use); NR == 0 reads it from `nrep`. One workgroup past the
+// vector range, launched when head + tail > 0, steps the `head` elements
+// just before element 0 and the `tail` elements after the last vector one
+// by one, so a shard takes one launch whatever its alignment.
 template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
                 float *__restrict__ mom, float *__restrict__ var,
-                void *__restrict__ out, int64_t nvec, ScalarArg<DS> sa) {
+                void *__restrict__ out, int64_t nvec, int head, int tail, ScalarArg<DS> sa) {
     const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
+    if ((int64_t)blockIdx.x * kBlock >= nvec) {
+        for (int k = threadIdx.x; k < head + tail; k += kBlock) {
+            const int64_t e = k < head ? (int64_t)(k - head) : nvec * kVec + (k - head);
+            step_one<NR, GB, PB>(reps, n, master, mom, var, out, e, sc);
+        }
+        return;
+    }
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
     const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
     if (j < nvec) step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
 }
 
-// One element i of the fused step (any alignment).
-template <int NR, bool GB, bool PB>
-__device__ __forceinline__ void step_one(const Reps<NR> &reps, int n, float *__restrict__ master,
+template <int NR, bool GB, bool PB, class R>
+__device__ __forceinline__ void step_one(const R &reps, int n, float *__restrict__ master,
                                          float *__restrict__ mom, float *__restrict__ var,
                                          void *__restrict__ out, int64_t i, const StepScalars &sc) {
+    constexpr int es = GB ? 2 : 4;
     float s;
-    if (GB) s = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[0])[i]);
-    else s = reinterpret_cast<const float *>(reps.p[0])[i];
+    if (GB) s = widen_bf16(reinterpret_cast<const uint16_t *>(rep_base(reps, 0, es))[i]);
+    else s = reinterpret_cast<const float *>(rep_base(reps, 0, es))[i];
     for (int q = 1; q < n; ++q) {
         float x;
-        if (GB) x = widen_bf16(reinterpret_cast<const uint16_t *>(reps.p[q])[i]);
-        else x = reinterpret_cast<const float *>(reps.p[q])[i];
+        if (GB) x = widen_bf16(reinterpret_cast<const uint16_t *>(rep_base(reps, q, es))[i]);
+        else x = reinterpret_cast<const float *>(rep_base(reps, q, es))[i];
         s = s + x;
     }
     float p = master[i], m = mom[i], v = var[i];
@@ -356,6 +378,11 @@ struct ShiftReps {
     const void *p[NR > 0 ? NR : ZERO_MAX_WORLD];
     uint8_t d[NR > 0 ? NR : ZERO_MAX_WORLD];
 };
+
+template <int NR>
+__device__ __forceinline__ const void *rep_base(const ShiftReps<NR> &r, int q, int es) {
+    return static_cast<const char *>(r.p[q]) + (int)r.d[q] * es;
+}
 
 // Value of v in the next lane of the wavefront (DPP wave shift left by one;
 // lanes without a next lane get 0 and do not use it).
@@ -533,9 +560,16 @@ template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
                   float *__restrict__ mom, float *__restrict__ var, void *__restrict__ out,
-                  int dout, int64_t nvec, ScalarArg<DS> sa) {
+                  int dout, int64_t nvec, int head, int tail, ScalarArg<DS> sa) {
     const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
+    if ((int64_t)blockIdx.x * kBlock >= nvec) {      // head and tail, as step_vec_kernel
+        for (int k = threadIdx.x; k < head + tail; k += kBlock) {
+            const int64_t e = k < head ? (int64_t)(k - head) : nvec * kVec + (k - head);
+            step_one<NR, GB, PB>(reps, n, master, mom, var, out, e, sc);
+        }
+        return;
+    }
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
     const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
@@ -689,28 +723,28 @@ hipError_t launch_fsdp_dtype(const FsdpArgs &a, hipStream_t stream) {
 }
 
 template <int NR, bool GB, bool PB, bool DS>
-hipError_t launch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
+hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail, hipStream_t stream) {
     Reps<NR> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
-    const int64_t grid = (nvec + kBlock - 1) / kBlock;
+    const int64_t grid = (nvec + kBlock - 1) / kBlock + (head + tail > 0 ? 1 : 0);
     // a dispatch holds at most 2^32-1 work-items
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
-                       ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec,
+                       ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, head, tail,
                        scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
 template <bool GB, bool PB, bool DS>
-hipError_t dispatch_vec(const StepArgs &a, int64_t nvec, hipStream_t stream) {
+hipError_t dispatch_vec(const StepArgs &a, int64_t nvec, int head, int tail, hipStream_t stream) {
     switch (a.n) {
-    case 1: return launch_vec<1, GB, PB, DS>(a, nvec, stream);
-    case 2: return launch_vec<2, GB, PB, DS>(a, nvec, stream);
-    case 4: return launch_vec<4, GB, PB, DS>(a, nvec, stream);
-    case 8: return launch_vec<8, GB, PB, DS>(a, nvec, stream);
-    case 16: return launch_vec<16, GB, PB, DS>(a, nvec, stream);
-    case 64: return launch_vec<64, GB, PB, DS>(a, nvec, stream);
-    default: return launch_vec<0, GB, PB, DS>(a, nvec, stream);
+    case 1: return launch_vec<1, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 2: return launch_vec<2, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 4: return launch_vec<4, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 8: return launch_vec<8, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 16: return launch_vec<16, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 64: return launch_vec<64, GB, PB, DS>(a, nvec, head, tail, stream);
+    default: return launch_vec<0, GB, PB, DS>(a, nvec, head, tail, stream);
     }
 }
 
@@ -793,7 +827,7 @@ inline int shifted_head(const StepArgs &a) {
 }
 
 template <int NR, bool GB, bool PB, bool DS>
-hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stream) {
+hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, int tail, hipStream_t stream) {
     const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
     ShiftReps<NR> reps;
     for (int q = 0; q < a.n; ++q) {
@@ -803,50 +837,43 @@ hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stre
     }
     void *out = (char *)a.out + (int64_t)oe * h;
     const int dout = (int)(((uintptr_t)out % 16) / oe);
-    const int64_t grid = (nvec + kBlock - 1) / kBlock;
+    const int64_t grid = (nvec + kBlock - 1) / kBlock + (h + tail > 0 ? 1 : 0);
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_shift_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
                        ZK_STEP_LDS, stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
-                       nvec, scalar_arg<DS>(a.sc, a.sc_dev));
+                       nvec, h, tail, scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
 template <bool GB, bool PB, bool DS>
-hipError_t dispatch_shift(const StepArgs &a, int h, int64_t nvec, hipStream_t stream) {
+hipError_t dispatch_shift(const StepArgs &a, int h, int64_t nvec, int tail, hipStream_t stream) {
     switch (a.n) {
-    case 1: return launch_shift<1, GB, PB, DS>(a, h, nvec, stream);
-    case 2: return launch_shift<2, GB, PB, DS>(a, h, nvec, stream);
-    case 4: return launch_shift<4, GB, PB, DS>(a, h, nvec, stream);
-    case 8: return launch_shift<8, GB, PB, DS>(a, h, nvec, stream);
-    case 16: return launch_shift<16, GB, PB, DS>(a, h, nvec, stream);
-    case 64: return launch_shift<64, GB, PB, DS>(a, h, nvec, stream);
-    default: return launch_shift<0, GB, PB, DS>(a, h, nvec, stream);
+    case 1: return launch_shift<1, GB, PB, DS>(a, h, nvec, tail, stream);
+    case 2: return launch_shift<2, GB, PB, DS>(a, h, nvec, tail, stream);
+    case 4: return launch_shift<4, GB, PB, DS>(a, h, nvec, tail, stream);
+    case 8: return launch_shift<8, GB, PB, DS>(a, h, nvec, tail, stream);
+    case 16: return launch_shift<16, GB, PB, DS>(a, h, nvec, tail, stream);
+    case 64: return launch_shift<64, GB, PB, DS>(a, h, nvec, tail, stream);
+    default: return launch_shift<0, GB, PB, DS>(a, h, nvec, tail, stream);
     }
 }
 
-// Element head [0, h), vector range, element tail.
+// Element head [0, h), vector range and element tail, in one launch.
 template <bool GB, bool PB, bool DS>
 hipError_t step_shifted(const StepArgs &a, int h, hipStream_t stream) {
     const int64_t nvec = (a.shard - h) / kVec;
-    if (h > 0) {
-        hipError_t e = launch_elem<GB, PB, DS>(a, 0, h, stream);
-        if (e != hipSuccess) return e;
-    }
-    hipError_t e = dispatch_shift<GB, PB, DS>(a, h, nvec, stream);
-    if (e != hipSuccess) return e;
-    const int64_t done = h + nvec * kVec;
-    if (done < a.shard) return launch_elem<GB, PB, DS>(a, done, a.shard, stream);
-    return hipSuccess;
+    const int tail = (int)(a.shard - h - nvec * kVec);
+    return dispatch_shift<GB, PB, DS>(a, h, nvec, tail, stream);
 }
 
 template <bool GB, bool PB, bool DS>
 hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
-    // Vector path from the first element at which all streams are 16-byte
-    // aligned; the few elements before it and the ragged tail take the
-    // element path (same arithmetic). Buffers at mixed phases take the
-    // shifted vector path; only buffers that are not naturally aligned, or
-    // shards shorter than the head plus one vector, run on the element path
-    // alone.
+    // Vector path from the head h that common_head chooses; the h elements
+    // before it and the ragged tail take the element step (same arithmetic)
+    // in one extra workgroup of the same launch. Buffers at mixed phases
+    // take the shifted vector path; only buffers that are not naturally
+    // aligned, or shards shorter than the head plus one vector, run on the
+    // element path alone.
     const int h = common_head(a);
     if (h < 0) {
         const int hs = shifted_head(a);
@@ -855,10 +882,7 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     }
     if (a.shard - h < kVec) return launch_elem<GB, PB, DS>(a, 0, a.shard, stream);
     const int64_t nvec = (a.shard - h) / kVec;
-    if (h > 0) {
-        hipError_t e = launch_elem<GB, PB, DS>(a, 0, h, stream);
-        if (e != hipSuccess) return e;
-    }
+    const int tail = (int)(a.shard - h - nvec * kVec);
     StepArgs b = a;
     const void *shifted[ZERO_MAX_WORLD];
     const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
@@ -868,11 +892,7 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     b.m = a.m + h;
     b.v = a.v + h;
     b.out = (char *)a.out + (int64_t)oe * h;
-    hipError_t e = dispatch_vec<GB, PB, DS>(b, nvec, stream);
-    if (e != hipSuccess) return e;
-    const int64_t done = h + nvec * kVec;
-    if (done < a.shard) return launch_elem<GB, PB, DS>(a, done, a.shard, stream);
-    return hipSuccess;
+    return dispatch_vec<GB, PB, DS>(b, nvec, h, tail, stream);
 }
 
 // ------------------------------------------------------------ segment copy
