@@ -1,6 +1,7 @@
-"""Buffers at mixed 16-byte phases: the shifted vector path.
+"""Buffers at mixed 16-byte phases: the shifted vector path, and launches
+whose blocks straddle 128-byte lines (dealt to the XCDs in groups).
 
-The state's phase is fixed by the library (lo mod 4 elements past a 256-byte
+The state's phase is fixed by the library (lo mod 32 elements past a 2 MiB
 boundary); replicas and output here sit at every element phase relative to
 it, each replica at its own phase. Every combination must give the oracle's
 values bit for bit, and the output must touch exactly its own elements
@@ -49,12 +50,12 @@ def _run_phases(world, rank, S, gdt, odt, combos, label):
     for t, (roffs, ooff) in enumerate(combos, start=1):
         reps, reps_h = [], []
         for q in range(world):
-            buf = torch.zeros(S + 16, dtype=gdt, device=dev)
+            buf = torch.zeros(S + 64, dtype=gdt, device=dev)
             g = buf[roffs[q]:roffs[q] + S]
             g[:valid] = synth.gaussian(valid, 1e-3, synth.grad_seed(t, q), gdt, dev)
             reps.append(g)
             reps_h.append(bits(g))
-        obuf = torch.full((S + 16,), SENTINEL, dtype=ivt, device=dev).view(odt)
+        obuf = torch.full((S + 64,), SENTINEL, dtype=ivt, device=dev).view(odt)
         out = obuf[ooff:ooff + S]
         st.step(reps, t, out)
         out_ref = np.zeros(S, np.uint16 if odt == torch.bfloat16 else np.float32)
@@ -106,3 +107,24 @@ def test_shifted_path_short_shards():
         combos = [((1, 2), 3), ((0, 5), 0), ((7, 7), 6)]
         _run_phases(2, 1, S, torch.bfloat16, torch.bfloat16, combos, f"short S={S}")
         log(f"short shard S={S} ok")
+
+
+def test_regrouped_blocks_large_shard():
+    """Launches whose streams straddle 128-byte lines deal the vector blocks
+    to the XCDs in groups of 8 (whole runs of 64 workgroups only). A shard of
+    200,003 elements (391 workgroups: 6 whole runs and a partial one, plus
+    the head/tail workgroup) on both paths that regroup:
+      - rank 0, every buffer 16-byte aligned but off its line by 8, 24, 40
+        or 56 elements (the vector path's 16-byte tier);
+      - ranks 1 and 3, replicas and output at mixed 16-byte phases (the
+        shifted path)."""
+    S, world = 200_003, 4
+    _run_phases(world, 0, S, torch.bfloat16, torch.bfloat16,
+                [((8, 24, 40, 56), 8), ((8, 8, 8, 8), 24), ((56, 40, 24, 8), 40)],
+                "16-byte tier, regrouped")
+    for rank in (1, 3):
+        _run_phases(world, rank, S, torch.bfloat16, torch.bfloat16,
+                    [((1, 2, 3, 4), 5), ((0, 0, 0, 7), 3), ((7, 0, 7, 0), 0)],
+                    f"shifted, regrouped r{rank}")
+    _run_phases(world, 1, S, torch.float32, torch.float32,
+                [((1, 2, 3, 0), 1), ((0, 0, 0, 2), 3)], "shifted fp32, regrouped")
