@@ -134,3 +134,11 @@ def test_llama7b_list_full_size_subset():
     assert_state_parity(label, got, orc.state(), out_got, np.concatenate(outs_h))
     assert_bitexact_state(label, got, orc.state(), out_got, np.concatenate(outs_h))
     st.close()
+
+
+def test_zero_row_parameters():
+    """Parameters with no rows at all ((0,), (0, 5)) next to ordinary ones:
+    no rank holds any of them, and the rest steps as usual."""
+    shapes = [(0,), (9, 4), (0, 5), (3,), (130, 2)]
+    for rank in range(4):
+        _run(shapes, 4, rank, torch.bfloat16, torch.bfloat16, 2)

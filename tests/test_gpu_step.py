@@ -415,3 +415,32 @@ def test_flatten_windows(dtype):
     with pytest.raises(zero.ZeroError):
         st.flatten(srcs, one, window=(P - 2, 3))
     st.close()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_flatten_with_empty_tensors(dtype):
+    """Zero-element tensors anywhere in the list (first, between, last, a
+    (3, 0) matrix) take no room in the flat vector; flatten and unflatten
+    stay bit-exact and the step over that flat vector matches the oracle."""
+    dev = torch.device("cuda")
+    shapes = [(0,), (5,), (3, 0), (1,), (0,), (1000, 3), (7,), (0, 4)]
+    numel = synth.numel_of(shapes)
+    assert numel == 3013
+    st = zero.ShardState(numel, 4, 3, 1e-3)
+    P = st.padded
+    vals = synth.gaussian(numel, 1.0, 3, dtype).to(dev)
+    srcs = synth.split_to_shapes(vals, shapes)
+    assert [x.numel() for x in srcs] == [0, 5, 0, 1, 0, 3000, 7, 0]
+    out = torch.full((P,), -1, dtype=torch.int16 if dtype == torch.bfloat16 else torch.int32,
+                     device=dev).view(dtype)
+    st.flatten(srcs, out)
+    want = oracle.flatten([bits(x) for x in srcs], P, fill=0x5A)
+    assert bits(out).tobytes() == want.tobytes()
+    dsts = [torch.full_like(x, 7) for x in srcs]
+    st.unflatten(out, dsts)
+    for a, b in zip(dsts, srcs):
+        assert bits(a).tobytes() == bits(b).tobytes()
+    r = run_small_parity(numel, 4, 3, dtype, torch.bfloat16, 2, 1e-3, shapes=shapes,
+                         label=f"empty tensors {dtype}")
+    assert_bitexact_state("empty tensors", r["state"], r["ref"], r["out"], r["out_ref"])
+    st.close()
