@@ -220,3 +220,59 @@ def test_schedule_errors():
     with pytest.raises(zero.ZeroError) as e:
         zero.ShardState(1000, 2, 0, 1e-3, betas=(0.9, 0.99999999)).schedule(1)
     assert e.value.code == zero.ZERO_EUNSUPPORTED
+
+
+def test_scheduled_steps_on_every_path():
+    """The scheduled (device-scalar) instantiation of each launch path
+    against the oracle: the shifted vector path (replicas and output at
+    mixed 16-byte phases, grouped workgroup order), the vector path with a
+    head and a tail, the element path (a shard shorter than one vector),
+    and a graph replay of the shifted path."""
+    dev = torch.device("cuda")
+    # shifted path: rank 1 of 4, S = 200,003
+    S, world, rank = 200_003, 4, 1
+    numel = world * S - 1
+    st = zero.ShardState(numel, world, rank, 1e-3, BETAS, EPS)
+    orc = oracle.ShardOracle(numel, world, rank, 1e-3, BETAS, EPS)
+    p = synth.gaussian(S, synth.PARAM_STD, synth.PARAM_SEED, torch.float32, dev)
+    st.load_master(p, flat_offset=0)
+    orc.master[:] = bits(p)
+    bufs = [torch.zeros(S + 64, dtype=torch.bfloat16, device=dev) for _ in range(world)]
+    reps = [b[1 + 2 * q:1 + 2 * q + S] for q, b in enumerate(bufs)]       # phases 1, 3, 5, 7
+    obuf = torch.zeros(S + 64, dtype=torch.bfloat16, device=dev)
+    out = obuf[3:3 + S]
+    st.schedule(1)
+
+    def fill(t):
+        for q, r in enumerate(reps):
+            synth.fill_gaussian(r, 1e-3, synth.grad_seed(t, q))
+
+    def check(t):
+        out_ref = np.zeros(S, np.uint16)
+        orc.step([bits(r) for r in reps], t, out_ref, grad_offset=0, out_offset=0)
+        torch.cuda.synchronize()
+        assert_bitexact_state(f"shifted sched t={t}", gpu_state(st), [orc.master, orc.m, orc.v],
+                              bits(out), out_ref)
+
+    for t in (1, 2):
+        fill(t)
+        st.step_sched(reps, out)
+        check(t)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.step_sched(reps, out)
+    for t in (3, 4):
+        fill(t)
+        g.replay()
+        check(t)
+    del g
+    st.close()
+    # vector path with head and tail, and the element path
+    for numel, world, rank in ((100_003, 4, 3), (9, 2, 1), (3, 8, 0)):
+        st, orc, reps, out, valid = _setup(numel, world, rank, 1e-3)
+        st.schedule(1)
+        for t in (1, 2, 3):
+            _fill(reps, valid, t)
+            st.step_sched(reps, out)
+            _check(f"sched numel={numel}", st, orc, reps, out, t)
+        st.close()
