@@ -128,3 +128,42 @@ def test_regrouped_blocks_large_shard():
                     f"shifted, regrouped r{rank}")
     _run_phases(world, 1, S, torch.float32, torch.float32,
                 [((1, 2, 3, 0), 1), ((0, 0, 0, 2), 3)], "shifted fp32, regrouped")
+
+
+def test_arbitrary_bit_patterns_through_the_shifted_path():
+    """Replicas of random 16-bit patterns (every bf16 class: zeros,
+    subnormals, normals, infinities, NaNs) at mixed phases, output at an odd
+    phase: the realignment in registers and the narrow stores move bits, so
+    the result must match the oracle on every element (NaN against NaN
+    counting as equal)."""
+    dev = torch.device("cuda")
+    S, world, rank = 70_001, 4, 2
+    numel = world * S - 1
+    st = zero.ShardState(numel, world, rank, LR, BETAS, EPS)
+    orc = oracle.ShardOracle(numel, world, rank, LR, BETAS, EPS)
+    valid = min(S, numel - st.lo)
+    p = synth.gaussian(S, synth.PARAM_STD, synth.PARAM_SEED, torch.float32, dev)
+    p[valid:] = 0
+    st.load_master(p, flat_offset=0)
+    orc.master[:] = bits(p)
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    for t, (roffs, ooff) in enumerate([((1, 4, 6, 3), 5), ((7, 0, 2, 5), 1)], start=1):
+        reps = []
+        for q in range(world):
+            buf = torch.zeros(S + 64, dtype=torch.int16, device=dev)
+            g = buf[roffs[q]:roffs[q] + S]
+            g[:valid] = torch.randint(-32768, 32768, (valid,), generator=gen,
+                                      dtype=torch.int32).to(torch.int16).to(dev)
+            reps.append(g.view(torch.bfloat16))
+        obuf = torch.full((S + 64,), SENTINEL, dtype=torch.int16, device=dev)
+        out = obuf[ooff:ooff + S].view(torch.bfloat16)
+        st.step(reps, t, out)
+        out_ref = np.zeros(S, np.uint16)
+        orc.step([bits(r) for r in reps], t, out_ref, grad_offset=0, out_offset=0)
+        torch.cuda.synchronize()
+        whole = obuf.cpu().numpy()
+        assert np.all(whole[:ooff] == SENTINEL) and np.all(whole[ooff + S:] == SENTINEL)
+        assert_bitexact_state(f"bit patterns t={t}", gpu_state(st), [orc.master, orc.m, orc.v],
+                              bits(out), out_ref)
+        log(f"arbitrary bit patterns t={t}: matches the oracle")
+    st.close()
