@@ -30,9 +30,10 @@
  *   - Element counts are int64: shards of more than 2^31 elements are fine.
  *   - Device pointers need only bf16 (2-byte) or fp32 (4-byte) natural
  *     alignment. The step runs 16-byte vectors whatever the buffers'
- *     offsets; buffers at different 16-byte phases cost a few percent, and
- *     shards or ranges shorter than about 16 elements run element by
- *     element.
+ *     offsets, after a head of at most 63 elements that puts the streams on
+ *     128-byte lines where they share a phase; buffers at different phases
+ *     cost a few percent, and shards or ranges shorter than about 70
+ *     elements may run element by element.
  *   - The library owns the context and its master/m/v buffers; the caller
  *     owns every pointer it passes, and its streams.
  *   - Output buffers must not overlap any input of the same call (the
@@ -172,7 +173,7 @@ int zero_step(zero_ctx *ctx, const void *const *grad_replicas,
  * covering the shard with disjoint ranges gives results bit-identical to
  * one zero_step. Ranges launched on different streams must be disjoint;
  * the library does not order them. Any range start takes the vector path
- * after a head of at most 7 elements.
+ * after a head of at most 63 elements.
  * EINVAL: as zero_step, plus shard_begin < 0, count < 0 or
  * shard_begin + count > shard. count == 0 is a no-op. */
 int zero_step_range(zero_ctx *ctx, int64_t shard_begin, int64_t count,
