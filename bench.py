@@ -336,6 +336,11 @@ def build_inputs(w, dev):
     synth.fill_gaussian(p[:valid], synth.PARAM_STD, synth.PARAM_SEED)
     st.load_master(p, flat_offset=0)
     del p
+    # return the staging block, so the buffers below start on fresh
+    # 2 MiB-aligned segments instead of inside its halves (measured: a
+    # replica 512 bytes off a 4 KiB page costs the fused step)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
     def grad_fill(buf, q):
         synth.fill_gaussian(buf, w["std"], synth.grad_seed(1, q),
