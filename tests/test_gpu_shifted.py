@@ -28,10 +28,6 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _elems_per_16b(dtype):
-    return 16 // torch.tensor([], dtype=dtype).element_size()
-
-
 def _run_phases(world, rank, S, gdt, odt, combos, label):
     """One shard state; step t uses the t-th (replica offsets, output offset)
     combination, each replica a view at that element offset into a fresh
