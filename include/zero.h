@@ -32,8 +32,8 @@
  *     alignment. The step runs 16-byte vectors whatever the buffers'
  *     offsets, after a head of at most 63 elements that puts the streams on
  *     128-byte lines where they share a phase; buffers at different phases
- *     cost a few percent, and shards or ranges shorter than about 70
- *     elements may run element by element. Buffers whose slices start on
+ *     cost a few percent, and shards or ranges shorter than about 16
+ *     elements run element by element. Buffers whose slices start on
  *     4 KiB pages run fastest (each replica 512 bytes off its page costs
  *     about 0.4% of the step).
  *   - The library owns the context and its master/m/v buffers; the caller

@@ -384,8 +384,9 @@ step_elem_kernel(Reps<0> reps, int nrep, float *__restrict__ master,
 //
 // An output at another phase is written with 2-, 4- and 8-byte stores that
 // cover exactly the lane's elements (measured no slower than a cross-lane
-// realignment into whole blocks). fp32 replicas read the three aligned
-// blocks that cover a lane's 32 bytes.
+// realignment into whole blocks). An fp32 replica's 32 bytes span three
+// aligned blocks: the lane loads two and takes the third, the next lane's
+// first, across lanes in the same way.
 
 // Replica pointer table: each base 16-byte aligned, and d[q] the number of
 // elements between it and the replica's element 0 of the vector range.
@@ -425,12 +426,13 @@ __device__ __forceinline__ ShiftRaw<true> load_shift(const void *base, int d, in
 }
 
 __device__ __forceinline__ ShiftRaw<false> load_shift(const void *base, int d, int64_t j,
-                                                      bool, ShiftRaw<false> *) {
+                                                      bool self_next, ShiftRaw<false> *) {
     const float4 *p = reinterpret_cast<const float4 *>(base) + 2 * j;
     ShiftRaw<false> r;
     r.a = ld_f4<ZK_NT_GRAD>(p);
     r.b = ld_f4<ZK_NT_GRAD>(p + 1);
-    r.c = d ? ld_f4<ZK_NT_GRAD>(p + 2) : make_float4(0.f, 0.f, 0.f, 0.f);
+    r.c = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (d && self_next) r.c = ld_f4<ZK_NT_GRAD>(p + 2);
     return r;
 }
 
@@ -441,7 +443,15 @@ __device__ __forceinline__ void complete_shift(ShiftRaw<true> &r, int d, bool se
     if (!self_next) r.b = nb;
 }
 
-__device__ __forceinline__ void complete_shift(ShiftRaw<false> &, int, bool) {}
+// fp32: the third block is the next lane's first.
+__device__ __forceinline__ void complete_shift(ShiftRaw<false> &r, int d, bool self_next) {
+    if (!d) return;
+    const uint4 nb = next_lane(make_uint4(__float_as_uint(r.a.x), __float_as_uint(r.a.y),
+                                          __float_as_uint(r.a.z), __float_as_uint(r.a.w)));
+    if (!self_next)
+        r.c = make_float4(__uint_as_float(nb.x), __uint_as_float(nb.y), __uint_as_float(nb.z),
+                          __uint_as_float(nb.w));
+}
 
 // Four words (eight bf16) starting D elements into the 16 elements of c:
 // word k is bytes [2D + 4k, 2D + 4k + 4).
@@ -811,11 +821,12 @@ inline bool all_at(const StepArgs &a, int h, uintptr_t align) {
 }
 
 // Head of the vector path: the smallest h < 64 at which every stream sits
-// on a 128-byte line (*lines = true); failing that, the smallest h < 8 at
-// which every stream sits on a 16-byte boundary; -1 if neither exists.
+// on a 128-byte line and at least one vector follows (*lines = true);
+// failing that, the smallest h < 8 at which every stream sits on a 16-byte
+// boundary; -1 if neither exists.
 inline int common_head(const StepArgs &a, bool *lines) {
     *lines = true;
-    for (int h = 0; h < kLineHead; ++h)
+    for (int h = 0; h < kLineHead && a.shard - h >= kVec; ++h)
         if (all_at(a, h, kLine)) return h;
     *lines = false;
     for (int h = 0; h < kVec; ++h)
