@@ -204,6 +204,49 @@ def bucketed_graph_extras(st, reps, out, t0, sizes=(1 << 20, 1 << 22, 1 << 24),
     return res
 
 
+def overlap_extras(st, reps, out, t0, bucket=1 << 26, n=4096, gemms=12):
+    """Why buckets: the step is HBM-bound, a backward pass mostly MFMA-bound.
+    bf16 GEMMs (n x n x n) on one stream and the bucketed step on another,
+    timed alone and together."""
+    S = st.shard
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+    gs, ss = torch.cuda.Stream(), torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    t = [t0]
+
+    def run_gemms():
+        gs.wait_stream(cur)
+        with torch.cuda.stream(gs):
+            for _ in range(gemms):
+                torch.matmul(a, b, out=c)
+        cur.wait_stream(gs)
+
+    def run_steps():
+        ss.wait_stream(cur)
+        for b0 in range(0, S, bucket):
+            cnt = min(bucket, S - b0)
+            st.step_range(b0, cnt, [r[b0:] for r in reps], t[0], out, grad_offset=0,
+                          param_offset=b0, stream=ss)
+        cur.wait_stream(ss)
+        t[0] += 1
+
+    def both():
+        run_gemms()
+        run_steps()
+
+    ms_g = _time_ms(run_gemms, reps=3)
+    ms_s = _time_ms(run_steps, reps=3)
+    ms_b = _time_ms(both, reps=3)
+    tflops = 2.0 * n ** 3 * gemms / (ms_g * 1e-3) / 1e12
+    res = {"gemm": {"n": n, "count": gemms, "ms": ms_g, "tflops": tflops},
+           "bucketed_step_ms": ms_s, "together_ms": ms_b,
+           "hidden_fraction_of_step": (ms_g + ms_s - ms_b) / ms_s}
+    del a, b, c
+    return res
+
+
 def list_extras(dev):
     """Multi-tensor flatten and unflatten on the Llama-7B-shaped list
     (291 tensors, 6,738,415,616 bf16 elements)."""
@@ -459,6 +502,8 @@ def main():
             st, reps, out, n_total + 1, sizes=(1 << 20, 1 << 22, 1 << 24, 1 << 26))
         log("bucketed step, graph replay")
         extras["bucketed_step_graph"] = bucketed_graph_extras(st, reps, out, n_total + 100)
+        log("bucketed step beside bf16 GEMMs")
+        extras["bucketed_step_beside_gemm"] = overlap_extras(st, reps, out, n_total + 200)
 
     del inp, reps, out, own_tensors, own_flat
     st.close()
