@@ -512,9 +512,9 @@ def main():
     context = {}
     if not args.no_context:
         context["torch_copy_gbps"] = round(copy_ceiling(8 << 30), 1)
-        context["note"] = ("torch's own device-to-device copy of 8 GiB; the library's "
-                           "one-tensor flatten (kernels.flatten) is a plain copy too, "
-                           "and the faster of the two")
+        context["note"] = "torch's own device-to-device copy of 8 GiB" + (
+            "; the one-tensor flatten in kernels.flatten is a plain copy through the library"
+            if k1_bytes and ntensors == 1 else "")
     if default and not args.no_extras:
         log("tensor-list flatten/unflatten")
         extras["llama7b_list"] = list_extras(dev)
