@@ -444,3 +444,47 @@ def test_flatten_with_empty_tensors(dtype):
                          label=f"empty tensors {dtype}")
     assert_bitexact_state("empty tensors", r["state"], r["ref"], r["out"], r["out_ref"])
     st.close()
+
+
+def test_all_ranks_concurrently_on_separate_streams():
+    """Contexts are independent: the N = 4 ranks' contexts step at the same
+    time, each on its own stream, reading the same full flat replicas and
+    writing disjoint slices of one shared full flat output (the all-gather's
+    result). 3 steps of 400,013 elements (ragged shard, pad in rank 3);
+    every rank's state and the whole output equal the oracle bit for bit,
+    and the pad stays +0."""
+    dev = torch.device("cuda")
+    numel, world, steps = 400_013, 4, 3
+    states = [zero.ShardState(numel, world, r, 1e-3) for r in range(world)]
+    orcs = [oracle.ShardOracle(numel, world, r, 1e-3) for r in range(world)]
+    P = states[0].padded
+    p = torch.zeros(P, dtype=torch.float32, device=dev)
+    p[:numel] = synth.gaussian(numel, synth.PARAM_STD, synth.PARAM_SEED, torch.float32, dev)
+    for st, o in zip(states, orcs):
+        st.load_master(p)
+        o.load_master(bits(p))
+    streams = [torch.cuda.Stream() for _ in range(world)]
+    out = torch.zeros(P, dtype=torch.bfloat16, device=dev)
+    out_ref = np.zeros(P, np.uint16)
+    torch.cuda.synchronize()
+    for t in range(1, steps + 1):
+        reps = []
+        for q in range(world):
+            g = torch.zeros(P, dtype=torch.bfloat16, device=dev)
+            g[:numel] = synth.gaussian(numel, 1e-3, synth.grad_seed(t, q), torch.bfloat16, dev)
+            reps.append(g)
+        torch.cuda.synchronize()
+        for st, s in zip(states, streams):
+            st.step(reps, t, out, stream=s)
+        reps_h = [bits(g) for g in reps]
+        for o in orcs:
+            o.step(reps_h, t, out_ref)
+        torch.cuda.synchronize()
+        assert bits(out).tobytes() == out_ref.tobytes(), f"shared output differs at t={t}"
+        for r, (st, o) in enumerate(zip(states, orcs)):
+            assert_bitexact_state(f"concurrent rank {r} t={t}", gpu_state(st),
+                                  [o.master, o.m, o.v], None, None)
+        assert not np.any(out_ref[numel:])
+        log(f"concurrent ranks: step {t} bit-exact")
+    for st in states:
+        st.close()
