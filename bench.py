@@ -154,12 +154,11 @@ def bucketed_extras(st, reps, out, t0, sizes=(1 << 22, 1 << 24, 1 << 26), nstrea
     t = [t0]
 
     def run(bucket):
-        for i, b0 in enumerate(range(0, S, bucket)):
-            cnt = min(bucket, S - b0)
-            s = streams[i % nstreams]
+        for s in streams:
             s.wait_stream(cur)
-            st.step_range(b0, cnt, [r[b0:] for r in reps], t[0], out, grad_offset=0,
-                          param_offset=b0, stream=s)
+        for i, b0 in enumerate(range(0, S, bucket)):
+            st.step_range(b0, min(bucket, S - b0), reps, t[0], out, grad_offset=b0,
+                          param_offset=b0, stream=streams[i % nstreams])
         for s in streams:
             cur.wait_stream(s)
         t[0] += 1
@@ -226,8 +225,7 @@ def overlap_extras(st, reps, out, t0, bucket=1 << 26, n=4096, gemms=12):
     def run_steps():
         ss.wait_stream(cur)
         for b0 in range(0, S, bucket):
-            cnt = min(bucket, S - b0)
-            st.step_range(b0, cnt, [r[b0:] for r in reps], t[0], out, grad_offset=0,
+            st.step_range(b0, min(bucket, S - b0), reps, t[0], out, grad_offset=b0,
                           param_offset=b0, stream=ss)
         cur.wait_stream(ss)
         t[0] += 1
