@@ -19,6 +19,11 @@ the same workload on this host.
 `--workload` times one of the other shards instead (the 1,000,003-element,
 GPT-2-small, Llama-13B and 70e9/N=64 cases, built as in the parity tests);
 those lines carry no CPU baseline and no extras.
+
+The default workload also times extras, each selectable with `--extras`:
+the bucketed step eager on 2 streams (buckets), replayed from a HIP graph
+(graph), beside bf16 GEMMs (gemm), the Llama-7B tensor-list flatten and
+unflatten (lists), and the per-parameter dim-0 layout step (fsdp).
 """
 from __future__ import annotations
 
@@ -136,6 +141,23 @@ def _time_ms(fn, reps=5):
     fn()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _time_ms_steady(fn, reps=5):
+    """Per-call GPU time once calls are queued back to back: one call is in
+    flight before the first event, so the host work of each later call
+    overlaps the GPU work of the one before (as in a training loop). For
+    calls whose host side is not negligible against their GPU time."""
+    fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
     a.record()
     for _ in range(reps):
         fn()
@@ -297,9 +319,15 @@ def fsdp_extras(dev, steps=5):
     def one():
         st.step(grads, t[0], outs)
         t[0] += 1
-    ms = _time_ms(one, reps=steps)
+    one()
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    one()                       # host side of a call: checks, pointer table, 10 launches
+    host_ms = (time.perf_counter() - h0) * 1e3
+    ms = _time_ms_steady(one, reps=steps)
     res = {"tensors": len(shapes), "local_elements": local, "ms": ms,
-           "gbps": step_bytes_per_elem(WORLD) * local / (ms * 1e-3) / 1e9}
+           "gbps": step_bytes_per_elem(WORLD) * local / (ms * 1e-3) / 1e9,
+           "host_ms_per_call": host_ms}
     del grads, outs
     st.close()
     torch.cuda.empty_cache()
@@ -323,6 +351,8 @@ def copy_ceiling(nbytes: int, reps: int = 5):
     torch.cuda.empty_cache()
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
+
+EXTRAS = ("buckets", "graph", "gemm", "lists", "fsdp")
 
 WORKLOADS = {
     "flat7b_n8_rank0": dict(
@@ -433,7 +463,14 @@ def main():
                     help="skip the plain-copy context measurement")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the bucketed-step and tensor-list measurements")
+    ap.add_argument("--extras", default=",".join(EXTRAS),
+                    help="comma-separated subset of the default workload's extra "
+                         "measurements to run: " + ", ".join(EXTRAS))
     args = ap.parse_args()
+    chosen = set() if args.no_extras else {e for e in args.extras.split(",") if e}
+    unknown = chosen - set(EXTRAS)
+    if unknown:
+        ap.error(f"unknown extras: {', '.join(sorted(unknown))}")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one rank's shard step on one GPU; runs on more than one "
               "GPU are not supported (the other ranks are simulated as gradient replicas "
@@ -494,12 +531,16 @@ def main():
     assert torch.isfinite(out[:max(0, min(S, numel - lo))].float()).all().item()
 
     extras = {}
-    if default and not args.no_extras:
+    if not default:
+        chosen = set()
+    if "buckets" in chosen:
         log("bucketed step")
         extras["bucketed_step_2_streams"] = bucketed_extras(
             st, reps, out, n_total + 1, sizes=(1 << 20, 1 << 22, 1 << 24, 1 << 26))
+    if "graph" in chosen:
         log("bucketed step, graph replay")
         extras["bucketed_step_graph"] = bucketed_graph_extras(st, reps, out, n_total + 100)
+    if "gemm" in chosen:
         log("bucketed step beside bf16 GEMMs")
         extras["bucketed_step_beside_gemm"] = overlap_extras(st, reps, out, n_total + 200)
 
@@ -513,9 +554,10 @@ def main():
         context["note"] = "torch's own device-to-device copy of 8 GiB" + (
             "; the one-tensor flatten in kernels.flatten is a plain copy through the library"
             if k1_bytes and ntensors == 1 else "")
-    if default and not args.no_extras:
+    if "lists" in chosen:
         log("tensor-list flatten/unflatten")
         extras["llama7b_list"] = list_extras(dev)
+    if "fsdp" in chosen:
         log("per-parameter (dim-0) layout step")
         extras["fsdp_llama7b_n8_rank0"] = fsdp_extras(dev)
 

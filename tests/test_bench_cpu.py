@@ -35,3 +35,10 @@ def test_workloads_cover_the_shard_configurations():
     assert w["llama13b_n8_rank7"]["rank"] == 7 and w["llama13b_n8_rank7"]["outliers"]
     assert w["flat1m_n4_rank3"]["numel"] == 1_000_003
     assert w["gpt2s_n8_rank3"]["shapes"] == "gpt2"
+
+
+def test_unknown_extras_are_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--extras", "fsdp,nope"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2 and "unknown extras: nope" in r.stderr
+    assert set(bench.EXTRAS) == {"buckets", "graph", "gemm", "lists", "fsdp"}
