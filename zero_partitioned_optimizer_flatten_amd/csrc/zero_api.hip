@@ -701,6 +701,7 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
     a.sc = make_scalars(c, mode == kHostT ? t : 1);
     a.sc_dev = mode == kHostT ? nullptr : c->sc_dev;
     a.num_cus = c->num_cus;
+    a.stream_state = zk::state_streams(c->shard);
     hipError_t e = zk::launch_step(a, stream);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "step launch");
 }

@@ -41,7 +41,15 @@ struct StepArgs {
     StepScalars sc;
     const StepScalars *sc_dev;
     int num_cus;
+    // Non-temporal hints on master/m/v in the vector path. Set when the
+    // context's whole state, not just this launch's range, is larger than
+    // the Infinity Cache: it cannot stay cached from one step to the next.
+    bool stream_state;
 };
+// MI355X's last-level (Infinity) cache in front of HBM.
+constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;
+// Whether a state of `elems` fp32 master/m/v elements is streamed.
+inline bool state_streams(int64_t elems) { return elems * 12 > kInfinityCacheBytes; }
 hipError_t launch_step(const StepArgs &a, hipStream_t stream);
 
 // Resolve the scalars of the schedule's current step into *out: `base`
