@@ -523,6 +523,7 @@ static int fsdp_step_common(zero_ctx *c, const void *const *grads, int32_t n_rep
     a.v = c->v;
     a.sc = make_scalars(c, mode == kHostT ? t : 1);
     a.sc_dev = mode == kHostT ? nullptr : c->sc_dev;
+    a.stream_state = zk::state_streams(c->shard);
     hipError_t e = zk::launch_fsdp_step(a, stream);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "per-parameter step launch");
 }

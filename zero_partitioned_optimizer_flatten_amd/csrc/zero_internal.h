@@ -77,6 +77,7 @@ struct FsdpArgs {
     float *master, *m, *v;
     StepScalars sc;
     const StepScalars *sc_dev;    // as in StepArgs
+    bool stream_state;            // as in StepArgs
 };
 hipError_t launch_fsdp_step(const FsdpArgs &a, hipStream_t stream);
 

@@ -814,9 +814,10 @@ step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
 // Each segment is one parameter's local row shard: its replica pointers
 // (already at this rank's first row), its output shard, and its place in
 // the rank's master/m/v. A workgroup takes one kBlock*8-element chunk of
-// one segment; segments whose streams are all 16-byte aligned use the
-// vector step, the rest (and every segment's last partial vector) the
-// element step.
+// one segment. In segments whose streams are all 16-byte aligned, a full
+// chunk takes the split lane layout and a partial one the vector step on
+// its whole vectors; the rest, and every segment's last partial vector,
+// take the element step.
 // Segments per launch: as many as keep the table within 4 KiB of kernel
 // arguments (32 with up to 8 replica pointers each, 16 with 16).
 constexpr int fsdp_batch(int nr) { return nr <= 8 ? 32 : 16; }
@@ -837,7 +838,8 @@ static_assert(sizeof(FsdpBatch<8>) <= 4096 && sizeof(FsdpBatch<kFsdpMaxWorld>) <
 template <int NR, bool EXACT, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 fsdp_step_kernel(FsdpBatch<NR> b, int nrep, float *__restrict__ master,
-                 float *__restrict__ mom, float *__restrict__ var, ScalarArg<DS> sa) {
+                 float *__restrict__ mom, float *__restrict__ var, int nt_state,
+                 ScalarArg<DS> sa) {
     const StepScalars sc = scalars(sa);
     const int64_t w = blockIdx.x;
     int lo = 0, hi = b.nseg - 1;                 // last segment with blk0 <= w
@@ -858,7 +860,16 @@ fsdp_step_kernel(FsdpBatch<NR> b, int nrep, float *__restrict__ master,
     const Reps<NR> &reps = b.reps[sgi];
     bool aligned = ((uintptr_t)out % 16) == 0 && ((uintptr_t)ms % 16) == 0;
     for (int q = 0; q < n; ++q) aligned = aligned && ((uintptr_t)reps.p[q] % 16) == 0;
-    const int64_t j = (w - b.blk0[sgi]) * kBlock + threadIdx.x;     // vector index
+    const int64_t chunk = w - b.blk0[sgi];
+    if (aligned && (chunk + 1) * kBlock * kVec <= numel) {
+        const int64_t q0 = chunk * 2 * kBlock + threadIdx.x;
+        if (nt_state)
+            step_vector_split<NR, GB, PB, true>(reps, n, pow2, ms, mm, vs, out, q0, sc);
+        else
+            step_vector_split<NR, GB, PB, false>(reps, n, pow2, ms, mm, vs, out, q0, sc);
+        return;
+    }
+    const int64_t j = chunk * kBlock + threadIdx.x;     // vector index
     if (j * kVec >= numel) return;
     if (aligned && (j + 1) * kVec <= numel) {
         step_vector<NR, GB, PB>(reps, n, pow2, ms, mm, vs, out, j, sc);
@@ -903,7 +914,7 @@ hipError_t launch_fsdp_typed(const FsdpArgs &a, hipStream_t stream) {
         if (blocks > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((fsdp_step_kernel<NR, EXACT, GB, PB, DS>), dim3((unsigned)blocks),
                            dim3(kBlock), ZK_STEP_LDS, stream, b, a.n, a.master, a.m, a.v,
-                           scalar_arg<DS>(a.sc, a.sc_dev));
+                           a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
