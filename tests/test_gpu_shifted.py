@@ -1,5 +1,5 @@
 """Buffers at mixed 16-byte phases: the shifted vector path, and launches
-whose blocks straddle 128-byte lines (dealt to the XCDs in groups).
+whose blocks straddle 128-byte lines.
 
 The state's phase is fixed by the library (lo mod 32 elements past a 2 MiB
 boundary); replicas and output here sit at every element phase relative to
@@ -105,11 +105,10 @@ def test_shifted_path_short_shards():
         log(f"short shard S={S} ok")
 
 
-def test_regrouped_blocks_large_shard():
-    """Launches whose streams straddle 128-byte lines deal the vector blocks
-    to the XCDs in groups of 8 (whole runs of 64 workgroups only). A shard of
-    200,003 elements (391 workgroups: 6 whole runs and a partial one, plus
-    the head/tail workgroup) on both paths that regroup:
+def test_line_straddling_blocks_large_shard():
+    """Launches whose streams straddle 128-byte lines, on a shard of 200,003
+    elements (390 full wavefront blocks in the split lane layout, a partial
+    block and the head/tail workgroup):
       - rank 0, every buffer 16-byte aligned but off its line by 8, 24, 40
         or 56 elements (the vector path's 16-byte tier);
       - ranks 1 and 3, replicas and output at mixed 16-byte phases (the
@@ -117,13 +116,13 @@ def test_regrouped_blocks_large_shard():
     S, world = 200_003, 4
     _run_phases(world, 0, S, torch.bfloat16, torch.bfloat16,
                 [((8, 24, 40, 56), 8), ((8, 8, 8, 8), 24), ((56, 40, 24, 8), 40)],
-                "16-byte tier, regrouped")
+                "16-byte tier")
     for rank in (1, 3):
         _run_phases(world, rank, S, torch.bfloat16, torch.bfloat16,
                     [((1, 2, 3, 4), 5), ((0, 0, 0, 7), 3), ((7, 0, 7, 0), 0)],
-                    f"shifted, regrouped r{rank}")
+                    f"shifted r{rank}")
     _run_phases(world, 1, S, torch.float32, torch.float32,
-                [((1, 2, 3, 0), 1), ((0, 0, 0, 2), 3)], "shifted fp32, regrouped")
+                [((1, 2, 3, 0), 1), ((0, 0, 0, 2), 3)], "shifted fp32")
 
 
 def test_arbitrary_bit_patterns_through_the_shifted_path():

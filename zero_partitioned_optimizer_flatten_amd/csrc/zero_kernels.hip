@@ -432,19 +432,6 @@ __device__ __forceinline__ void step_vector_split(const Reps<NR> &reps, int n, b
     }
 }
 
-// Logical vector block of workgroup b, for launches in which some stream's
-// wavefront blocks straddle 128-byte lines: within each run of 64
-// workgroups, which the hardware deals to the 8 XCDs in turn, XCD x takes 8
-// consecutive blocks, so most lines shared by adjacent blocks stay in one
-// L2 instead of being fetched, or written, by two. (Measured: 4.8% faster
-// on the Llama-13B rank-7 mixed layout, 3% with replicas one element off;
-// no gain when every stream is line-aligned, so those launches keep the
-// hardware order.)
-__device__ __forceinline__ int64_t xcd_block(int64_t b, int64_t nblk) {
-    if (b >= nblk / 64 * 64) return b;
-    return (b & ~(int64_t)63) | ((b & 7) << 3) | ((b >> 3) & 7);
-}
-
 // One element i of the fused step (any alignment). R is a replica table:
 // rep_base(reps, q, element size) gives replica q's element 0.
 template <int NR, bool GB, bool PB, class R>
@@ -469,8 +456,8 @@ template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
                 float *__restrict__ mom, float *__restrict__ var,
-                void *__restrict__ out, int64_t nvec, int head, int tail, int regroup,
-                int nt_state, ScalarArg<DS> sa) {
+                void *__restrict__ out, int64_t nvec, int head, int tail, int nt_state,
+                ScalarArg<DS> sa) {
     const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
     if ((int64_t)blockIdx.x * kBlock >= nvec) {
@@ -482,8 +469,7 @@ step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
     }
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
-    const int64_t vb = regroup ? xcd_block(blockIdx.x, (nvec + kBlock - 1) / kBlock)
-                               : (int64_t)blockIdx.x;
+    const int64_t vb = blockIdx.x;
     if ((vb + 1) * kBlock <= nvec) {
         const int64_t q0 = vb * 2 * kBlock + threadIdx.x;
         if (nt_state)
@@ -746,6 +732,196 @@ __device__ __forceinline__ void store_f32x8_at(float *q, int d, const float (&x)
     }
 }
 
+// ---- split lane layout on the shifted path (full wavefront blocks)
+// Lane l owns the quads l and l + kBlock of the block, as in the vector
+// path. A replica is read in 4-element units: 8 bytes of bf16, 16 bytes of
+// fp32. A replica d elements past its 16-byte base starts its quads r =
+// d mod 4 elements into a unit, so a lane's quad spans its own unit and
+// the next. The next unit of half 0 and of half 1 is the next lane's (DPP
+// wave shift); lane 63 loads both of its next units itself: the block's
+// second half starts there, and past it the unit holds the block's last
+// element, so no read leaves the units of the buffer's own elements.
+template <bool GB> struct UnitT;
+template <> struct UnitT<true> { typedef uint2 T; };
+template <> struct UnitT<false> { typedef uint4 T; };
+
+__device__ __forceinline__ uint2 next_lane(uint2 v) {
+    return make_uint2(next_lane(v.x), next_lane(v.y));
+}
+
+template <bool GB>
+__device__ __forceinline__ typename UnitT<GB>::T load_unit(const void *base, int64_t u) {
+    if constexpr (GB) {
+        const uint2 *p = reinterpret_cast<const uint2 *>(base) + u;
+        if (ZK_NT_GRAD) {
+            u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+            return make_uint2(v.x, v.y);
+        }
+        return *p;
+    } else {
+        return ld_u4<ZK_NT_GRAD>(reinterpret_cast<const uint4 *>(base) + u);
+    }
+}
+
+template <bool GB> struct ShiftUnits {
+    typename UnitT<GB>::T a[2], nx[2];     // own unit and next unit of each half
+};
+
+// Four elements starting r elements into unit a (then nx).
+__device__ __forceinline__ void take4(uint2 a, uint2 nx, int r, float *x) {
+    uint32_t w0, w1;
+    switch (r) {
+    case 0: w0 = a.x; w1 = a.y; break;
+    case 1: w0 = __builtin_amdgcn_alignbyte(a.y, a.x, 2);
+            w1 = __builtin_amdgcn_alignbyte(nx.x, a.y, 2); break;
+    case 2: w0 = a.y; w1 = nx.x; break;
+    default: w0 = __builtin_amdgcn_alignbyte(nx.x, a.y, 2);
+             w1 = __builtin_amdgcn_alignbyte(nx.y, nx.x, 2); break;
+    }
+    x[0] = widen_bf16(w0 & 0xFFFFu); x[1] = widen_bf16(w0 >> 16);
+    x[2] = widen_bf16(w1 & 0xFFFFu); x[3] = widen_bf16(w1 >> 16);
+}
+
+__device__ __forceinline__ void take4(uint4 a, uint4 nx, int r, float *x) {
+    const uint32_t c[8] = {a.x, a.y, a.z, a.w, nx.x, nx.y, nx.z, nx.w};
+    switch (r) {
+    case 0: x[0] = __uint_as_float(c[0]); x[1] = __uint_as_float(c[1]);
+            x[2] = __uint_as_float(c[2]); x[3] = __uint_as_float(c[3]); break;
+    case 1: x[0] = __uint_as_float(c[1]); x[1] = __uint_as_float(c[2]);
+            x[2] = __uint_as_float(c[3]); x[3] = __uint_as_float(c[4]); break;
+    case 2: x[0] = __uint_as_float(c[2]); x[1] = __uint_as_float(c[3]);
+            x[2] = __uint_as_float(c[4]); x[3] = __uint_as_float(c[5]); break;
+    default: x[0] = __uint_as_float(c[3]); x[1] = __uint_as_float(c[4]);
+             x[2] = __uint_as_float(c[5]); x[3] = __uint_as_float(c[6]); break;
+    }
+}
+
+template <int NR, bool GB>
+__device__ __forceinline__ void fold_group_split_shift(const ShiftReps<NR> &reps, int q0, int n,
+                                                       int64_t ub, float (&s)[kVec]) {
+    const int lane = threadIdx.x % 64;
+    ShiftUnits<GB> raw[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        if (q0 + k < n) {
+            const int d = reps.d[q0 + k];
+            const int64_t u = ub + (GB ? d / 4 : 0);
+            raw[k].a[0] = load_unit<GB>(reps.p[q0 + k], u);
+            raw[k].a[1] = load_unit<GB>(reps.p[q0 + k], u + kBlock);
+            if ((d & 3) && lane == 63) {
+                raw[k].nx[0] = load_unit<GB>(reps.p[q0 + k], u + 1);
+                raw[k].nx[1] = load_unit<GB>(reps.p[q0 + k], u + kBlock + 1);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+        if (q0 + k < n) {
+            const int r = reps.d[q0 + k] & 3;
+            if (r) {
+                const typename UnitT<GB>::T n0 = next_lane(raw[k].a[0]);
+                const typename UnitT<GB>::T n1 = next_lane(raw[k].a[1]);
+                if (lane != 63) {
+                    raw[k].nx[0] = n0;
+                    raw[k].nx[1] = n1;
+                }
+            } else {
+                raw[k].nx[0] = raw[k].a[0];
+                raw[k].nx[1] = raw[k].a[1];
+            }
+            float x[kVec];
+            take4(raw[k].a[0], raw[k].nx[0], r, x);
+            take4(raw[k].a[1], raw[k].nx[1], r, x + 4);
+            if (q0 + k == 0) {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) s[e] = x[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) s[e] = s[e] + x[e];
+            }
+        }
+    }
+}
+
+// Four bf16 (packed in x, y) to q, which sits d elements past an 8-byte
+// boundary (d = 0..3).
+__device__ __forceinline__ void store_bf16x4_at(uint16_t *q, int d, uint32_t x, uint32_t y) {
+    if (d == 0) {
+        st_nt(reinterpret_cast<u32x2_t *>(q), u32x2_t{x, y});
+    } else if (d == 2) {
+        st_nt(reinterpret_cast<uint32_t *>(q), x);
+        st_nt(reinterpret_cast<uint32_t *>(q) + 1, y);
+    } else {                                             // q + 1 is 4-byte aligned
+        st_nt(q, (uint16_t)(x & 0xFFFFu));
+        st_nt(reinterpret_cast<uint32_t *>(q + 1), __builtin_amdgcn_alignbyte(y, x, 2));
+        st_nt(q + 3, (uint16_t)(y >> 16));
+    }
+}
+
+// Four fp32 to q, which sits d elements past a 16-byte boundary.
+__device__ __forceinline__ void store_f32x4_at(float *q, int d, const float *x) {
+    if (d == 0) {
+        st_f4<ZK_NT_OUT>(q, make_float4(x[0], x[1], x[2], x[3]));
+    } else if (d == 2) {
+        st_nt(reinterpret_cast<f32x2_t *>(q), f32x2_t{x[0], x[1]});
+        st_nt(reinterpret_cast<f32x2_t *>(q + 2), f32x2_t{x[2], x[3]});
+    } else {                                             // q + 1 is 8-byte aligned
+        st_nt(q, x[0]);
+        st_nt(reinterpret_cast<f32x2_t *>(q + 1), f32x2_t{x[1], x[2]});
+        st_nt(q + 3, x[3]);
+    }
+}
+
+// Full block blk of the shifted path in the split lane layout.
+template <int NR, bool GB, bool PB, bool NTS>
+__device__ __forceinline__ void step_block_split_shift(const ShiftReps<NR> &reps, int n,
+                                                       bool pow2, float *__restrict__ master,
+                                                       float *__restrict__ mom,
+                                                       float *__restrict__ var,
+                                                       void *__restrict__ out, int dout,
+                                                       int64_t blk, const StepScalars &sc) {
+    const int64_t q0 = blk * 2 * kBlock + threadIdx.x;    // state quad of half 0
+    const int64_t ub = blk * 2 * kBlock + threadIdx.x;    // replica unit of half 0 at d = 0
+    float s[kVec];
+    if constexpr (NR > 0 && NR <= 2 * kGroup) {
+#pragma unroll
+        for (int r = 0; r < NR; r += kGroup) fold_group_split_shift<NR, GB>(reps, r, n, ub, s);
+    } else {
+#pragma unroll 1
+        for (int r = 0; r < n; r += kGroup) fold_group_split_shift<NR, GB>(reps, r, n, ub, s);
+    }
+    float p[kVec], m[kVec], v[kVec];
+    load8_split<NTS>(master, q0, p);
+    load8_split<NTS>(mom, q0, m);
+    load8_split<NTS>(var, q0, v);
+    float g[kVec];
+    if (pow2) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;
+    } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
+    }
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
+    store8_split<NTS>(master, q0, p);
+    store8_split<NTS>(mom, q0, m);
+    store8_split<NTS>(var, q0, v);
+    const int64_t e0 = 4 * q0, e1 = 4 * (q0 + kBlock);    // first element of each quad
+    if (PB) {
+        uint16_t *o = reinterpret_cast<uint16_t *>(out);
+        const int d = dout & 3;
+        store_bf16x4_at(o + e0, d, round_bf16(p[0]) | (round_bf16(p[1]) << 16),
+                        round_bf16(p[2]) | (round_bf16(p[3]) << 16));
+        store_bf16x4_at(o + e1, d, round_bf16(p[4]) | (round_bf16(p[5]) << 16),
+                        round_bf16(p[6]) | (round_bf16(p[7]) << 16));
+    } else {
+        float *o = reinterpret_cast<float *>(out);
+        store_f32x4_at(o + e0, dout, p);
+        store_f32x4_at(o + e1, dout, p + 4);
+    }
+}
+
 // Vector j of the shifted path: state aligned; replicas read through
 // their aligned bases; the output (element pointer of the range's first
 // element, dout elements past a 16-byte boundary) written at its phase.
@@ -753,7 +929,8 @@ template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
                   float *__restrict__ mom, float *__restrict__ var, void *__restrict__ out,
-                  int dout, int64_t nvec, int head, int tail, ScalarArg<DS> sa) {
+                  int dout, int64_t nvec, int head, int tail, int nt_state,
+                  ScalarArg<DS> sa) {
     const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
     if ((int64_t)blockIdx.x * kBlock >= nvec) {      // head and tail, as step_vec_kernel
@@ -763,9 +940,18 @@ step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
         }
         return;
     }
-    const int64_t blk = xcd_block(blockIdx.x, (nvec + kBlock - 1) / kBlock);
+    const int64_t blk = blockIdx.x;
     constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
     const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
+    if ((blk + 1) * kBlock <= nvec) {
+        if (nt_state)
+            step_block_split_shift<NR, GB, PB, true>(reps, n, pow2, master, mom, var, out, dout,
+                                                     blk, sc);
+        else
+            step_block_split_shift<NR, GB, PB, false>(reps, n, pow2, master, mom, var, out, dout,
+                                                      blk, sc);
+        return;
+    }
     const int64_t j = blk * kBlock + threadIdx.x;
     if (j >= nvec) return;
     const bool self_next = (threadIdx.x % 64) == 63 || j + 1 == nvec;
@@ -933,7 +1119,7 @@ hipError_t launch_fsdp_dtype(const FsdpArgs &a, hipStream_t stream) {
 }
 
 template <int NR, bool GB, bool PB, bool DS>
-hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail, int regroup,
+hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail,
                       hipStream_t stream) {
     Reps<NR> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
@@ -942,21 +1128,21 @@ hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail, int r
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
                        ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, head, tail,
-                       regroup, a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
+                       a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
 template <bool GB, bool PB, bool DS>
-hipError_t dispatch_vec(const StepArgs &a, int64_t nvec, int head, int tail, int regroup,
+hipError_t dispatch_vec(const StepArgs &a, int64_t nvec, int head, int tail,
                         hipStream_t stream) {
     switch (a.n) {
-    case 1: return launch_vec<1, GB, PB, DS>(a, nvec, head, tail, regroup, stream);
-    case 2: return launch_vec<2, GB, PB, DS>(a, nvec, head, tail, regroup, stream);
-    case 4: return launch_vec<4, GB, PB, DS>(a, nvec, head, tail, regroup, stream);
-    case 8: return launch_vec<8, GB, PB, DS>(a, nvec, head, tail, regroup, stream);
-    case 16: return launch_vec<16, GB, PB, DS>(a, nvec, head, tail, regroup, stream);
-    case 64: return launch_vec<64, GB, PB, DS>(a, nvec, head, tail, regroup, stream);
-    default: return launch_vec<0, GB, PB, DS>(a, nvec, head, tail, regroup, stream);
+    case 1: return launch_vec<1, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 2: return launch_vec<2, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 4: return launch_vec<4, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 8: return launch_vec<8, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 16: return launch_vec<16, GB, PB, DS>(a, nvec, head, tail, stream);
+    case 64: return launch_vec<64, GB, PB, DS>(a, nvec, head, tail, stream);
+    default: return launch_vec<0, GB, PB, DS>(a, nvec, head, tail, stream);
     }
 }
 
@@ -999,14 +1185,12 @@ inline bool all_at(const StepArgs &a, int h, uintptr_t align) {
 }
 
 // Head of the vector path: the smallest h < 64 at which every stream sits
-// on a 128-byte line and at least one vector follows (*lines = true);
-// failing that, the smallest h < 8 at which every stream sits on a 16-byte
-// boundary; -1 if neither exists.
-inline int common_head(const StepArgs &a, bool *lines) {
-    *lines = true;
+// on a 128-byte line and at least one vector follows; failing that, the
+// smallest h < 8 at which every stream sits on a 16-byte boundary; -1 if
+// neither exists.
+inline int common_head(const StepArgs &a) {
     for (int h = 0; h < kLineHead && a.shard - h >= kVec; ++h)
         if (all_at(a, h, kLine)) return h;
-    *lines = false;
     for (int h = 0; h < kVec; ++h)
         if (all_at(a, h, 16)) return h;
     return -1;
@@ -1056,7 +1240,7 @@ hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, int tail, hipStr
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_shift_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
                        ZK_STEP_LDS, stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
-                       nvec, h, tail, scalar_arg<DS>(a.sc, a.sc_dev));
+                       nvec, h, tail, a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
@@ -1089,8 +1273,7 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     // take the shifted vector path; only buffers that are not naturally
     // aligned, or shards shorter than the head plus one vector, run on the
     // element path alone.
-    bool lines = false;
-    const int h = common_head(a, &lines);
+    const int h = common_head(a);
     if (h < 0) {
         const int hs = shifted_head(a);
         if (hs >= 0 && a.shard - hs >= kVec) return step_shifted<GB, PB, DS>(a, hs, stream);
@@ -1108,7 +1291,7 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     b.m = a.m + h;
     b.v = a.v + h;
     b.out = (char *)a.out + (int64_t)oe * h;
-    return dispatch_vec<GB, PB, DS>(b, nvec, h, tail, lines ? 0 : 1, stream);
+    return dispatch_vec<GB, PB, DS>(b, nvec, h, tail, stream);
 }
 
 // ------------------------------------------------------------ segment copy
