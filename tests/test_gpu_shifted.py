@@ -1,7 +1,7 @@
 """Buffers at mixed 16-byte phases: the shifted vector path, and launches
 whose blocks straddle 128-byte lines.
 
-The state's phase is fixed by the library (lo mod 32 elements past a 2 MiB
+The state's phase is fixed by the library (lo mod 32 elements past a 1 MiB
 boundary); replicas and output here sit at every element phase relative to
 it, each replica at its own phase. Every combination must give the oracle's
 values bit for bit, and the output must touch exactly its own elements
