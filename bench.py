@@ -18,7 +18,9 @@ the same workload on this host.
 
 `--workload` times one of the other shards instead (the 1,000,003-element,
 GPT-2-small, Llama-13B and 70e9/N=64 cases, built as in the parity tests);
-those lines carry no CPU baseline and no extras.
+those lines carry no CPU baseline and no extras. The Llama-13B shard comes
+twice: with the peers' slices at address phase 0 (mixed 16-byte phases, the
+shifted path) and at the phase they have inside full flat buffers.
 
 The default workload also times extras, each selectable with `--extras`:
 the bucketed step eager on 2 streams (buckets), replayed from a HIP graph
@@ -375,6 +377,13 @@ WORKLOADS = {
              "slice only, bf16 output into the full flat buffer; 1% of gradients x100",
         numel=None, world=8, rank=7, shapes="llama13b", gdt=torch.bfloat16, std=1e-3,
         outliers=True, peers="slice", out="full", flatten=True),
+    "llama13b_n8_rank7_lo": dict(
+        desc="Llama-13B list + one scalar (364 tensors, 13,015,864,321 elements), N=8, rank 7 "
+             "(odd lo, 7 pad elements); own gradient flattened from the list, each peer's "
+             "slice stored at the address phase (lo mod 64 elements) it has in a full flat "
+             "buffer, bf16 output into the full flat buffer; 1% of gradients x100",
+        numel=None, world=8, rank=7, shapes="llama13b", gdt=torch.bfloat16, std=1e-3,
+        outliers=True, peers="slice_at_lo", out="full", flatten=True),
     "flat70b_n64_rank0": dict(
         desc="70e9-element flat vector, N=64, rank 0 shard of 1,093,750,000, slice-only "
              "replicas and output; flatten not timed (the full own gradient and its flat copy, "
@@ -436,6 +445,13 @@ def build_inputs(w, dev):
             buf = torch.zeros(P, dtype=gdt, device=dev)
             grad_fill(buf[lo:lo + valid], q)
             reps.append(buf[lo:lo + S])
+        elif w["peers"] == "slice_at_lo":
+            # the part of a full flat buffer that the step reads, at the
+            # offset within a 128-byte line that element lo has there
+            ph = lo % 64
+            buf = torch.zeros(S + 64, dtype=gdt, device=dev)
+            grad_fill(buf[ph:ph + valid], q)
+            reps.append(buf[ph:ph + S])
         else:
             buf = torch.zeros(S, dtype=gdt, device=dev)
             grad_fill(buf[:valid], q)

@@ -33,6 +33,9 @@ def test_workloads_cover_the_shard_configurations():
     assert (w["flat7b_n8_rank0"]["numel"], w["flat7b_n8_rank0"]["world"]) == (7_000_000_000, 8)
     assert (w["flat70b_n64_rank0"]["numel"], w["flat70b_n64_rank0"]["world"]) == (70_000_000_000, 64)
     assert w["llama13b_n8_rank7"]["rank"] == 7 and w["llama13b_n8_rank7"]["outliers"]
+    assert w["llama13b_n8_rank7_lo"]["peers"] == "slice_at_lo"
+    assert {k: v for k, v in w["llama13b_n8_rank7_lo"].items() if k not in ("peers", "desc")} \
+        == {k: v for k, v in w["llama13b_n8_rank7"].items() if k not in ("peers", "desc")}
     assert w["flat1m_n4_rank3"]["numel"] == 1_000_003
     assert w["gpt2s_n8_rank3"]["shapes"] == "gpt2"
 
