@@ -54,6 +54,21 @@ def test_gpt2_small_n8_rank3():
     assert_bitexact_state("gpt2s", r["state"], r["ref"], r["out"], r["out_ref"])
 
 
+@pytest.mark.parametrize("shard", [22_369_621, 22_369_622])
+def test_state_hints_on_both_sides_of_the_cache_size(shard):
+    """The launcher streams master/m/v (non-temporal loads and stores) when
+    the context's state, 12 B per shard element, exceeds 256 MiB, and keeps
+    the default cache policy otherwise. 22,369,621 elements are 268,435,452
+    bytes of state (default policy), one more element 268,435,464 (streamed):
+    both equal the oracle bit for bit. N = 2, rank 1 at an odd offset (a
+    head before the vector range), bf16 gradients and output, 2 steps."""
+    numel = 2 * shard - 1
+    log(f"state hints: shard={shard} state bytes={12 * shard}")
+    r = run_small_parity(numel, 2, 1, torch.bfloat16, torch.bfloat16, 2, 1e-3,
+                         label=f"state hints shard={shard}")
+    assert_bitexact_state(f"shard {shard}", r["state"], r["ref"], r["out"], r["out_ref"])
+
+
 # ------------------------------------------------- every replica count
 
 @pytest.mark.parametrize("world", [1, 2, 3, 4, 5, 7, 8, 16, 32, 64, 100, 256])
