@@ -84,13 +84,17 @@ def test_flat70b_n64_rank0_full_size():
     _slice_only_run(70_000_000_000, 64, 0, 3, "flat70b_n64")
 
 
-def test_llama13b_n8_last_rank_full_size():
+@pytest.mark.parametrize("peer_phase", ["zero", "lo"])
+def test_llama13b_n8_last_rank_full_size(peer_phase):
     """Llama-13B list + 1 scalar (364 tensors, 13,015,864,321 elements),
     N = 8, rank 7 (7 pad elements at the end of its slice, odd lo). This
     rank's own gradient is a real tensor list flattened by the HIP path into
-    a full padded vector; the seven peers hold this slice only. bf16
-    gradients N(0, 1e-3) with 1% of elements x100, bf16 output into the full
-    flat parameter buffer at offset lo, 5 steps."""
+    a full padded vector; the seven peers hold this slice only, either at
+    address phase 0 (mixed 16-byte phases: the shifted path) or at the
+    offset within a 128-byte line that element lo has in a full flat buffer
+    (every stream at the state's phase: the vector path). bf16 gradients
+    N(0, 1e-3) with 1% of elements x100, bf16 output into the full flat
+    parameter buffer at offset lo, 5 steps."""
     shapes = synth.llama_shapes(40, 5120, 13824, trailing_scalar=True)
     numel = synth.numel_of(shapes)
     assert len(shapes) == 364 and numel == 13_015_864_321
@@ -110,7 +114,9 @@ def test_llama13b_n8_last_rank_full_size():
     del p
     own_list_storage = torch.empty(numel, dtype=torch.bfloat16, device=dev)
     own_flat = torch.empty(P, dtype=torch.bfloat16, device=dev)
-    peers = [torch.zeros(S, dtype=torch.bfloat16, device=dev) for _ in range(world - 1)]
+    ph = lo % 64 if peer_phase == "lo" else 0
+    peers = [torch.zeros(S + 64, dtype=torch.bfloat16, device=dev)[ph:ph + S]
+             for _ in range(world - 1)]
     out = torch.zeros(P, dtype=torch.bfloat16, device=dev)
     out_ref = np.zeros(K, np.uint16)
     for t in range(1, 6):
@@ -124,15 +130,15 @@ def test_llama13b_n8_last_rank_full_size():
             assert torch.equal(own_flat[:numel].view(torch.int16),
                                own_list_storage.view(torch.int16))
             assert not torch.any(own_flat[numel:].view(torch.int16))
-            log("llama13b_n8: flatten of 364 tensors bit-exact")
+            log(f"llama13b_n8 peers@{peer_phase}: flatten of 364 tensors bit-exact")
         for k, q in enumerate(q for q in range(world) if q != rank):
             synth.fill_gaussian(peers[k][:valid], 1e-3, synth.grad_seed(t, q),
                                 synth.mask_seed(t, q))
         reps = peers[:rank] + [own_flat[lo:]] + peers[rank:]
         st.step(reps, t, out, grad_offset=0, param_offset=lo)
         orc.step([bits(r[idx]) for r in reps], t, out_ref, grad_offset=0, out_offset=0)
-        log(f"llama13b_n8: step {t} done")
-    _check_sampled("llama13b_n8", st, orc, idx, out, lo, out_ref)
+        log(f"llama13b_n8 peers@{peer_phase}: step {t} done")
+    _check_sampled(f"llama13b_n8 peers@{peer_phase}", st, orc, idx, out, lo, out_ref)
     tail = bits(st.get_state()[0][valid:])
     assert not np.any(tail.view(np.uint32)), "pad master not zero"
     st.close()
