@@ -77,6 +77,17 @@ constexpr int kGroup = 8;            // replicas loaded together
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+template <bool NT>
+__device__ __forceinline__ uint2 ld_u2(const void *p) {
+    if (NT) {
+        u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+        return make_uint2(v.x, v.y);
+    }
+    return *reinterpret_cast<const uint2 *>(p);
+}
 
 template <bool NT>
 __device__ __forceinline__ uint4 ld_u4(const void *p) {
@@ -281,8 +292,6 @@ __device__ __forceinline__ void step_vector(const Reps<NR> &reps, int n, bool po
     }
 }
 
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-
 // Split lane layout of a full wavefront block (kBlock vectors, 8*kBlock
 // elements): lane l owns the 4-element quads l and l + kBlock of the block,
 // so every load and store instruction of the wavefront covers one
@@ -293,11 +302,6 @@ template <bool GB> struct SplitRaw;
 template <> struct SplitRaw<true> { uint2 a, b; };
 template <> struct SplitRaw<false> { float4 a, b; };
 
-__device__ __forceinline__ uint2 ld_u2_nt(const void *p) {
-    u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
-    return make_uint2(v.x, v.y);
-}
-
 template <bool GB>
 __device__ __forceinline__ SplitRaw<GB> load_split(const void *base, int64_t q0);
 
@@ -305,13 +309,8 @@ template <>
 __device__ __forceinline__ SplitRaw<true> load_split<true>(const void *base, int64_t q0) {
     const uint2 *p = reinterpret_cast<const uint2 *>(base);
     SplitRaw<true> r;
-    if (ZK_NT_GRAD) {
-        r.a = ld_u2_nt(p + q0);
-        r.b = ld_u2_nt(p + q0 + kBlock);
-    } else {
-        r.a = p[q0];
-        r.b = p[q0 + kBlock];
-    }
+    r.a = ld_u2<ZK_NT_GRAD>(p + q0);
+    r.b = ld_u2<ZK_NT_GRAD>(p + q0 + kBlock);
     return r;
 }
 
@@ -687,8 +686,6 @@ __device__ __forceinline__ void st_nt(T *p, T v) {
     else *p = v;
 }
 
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // Eight packed bf16 values (o.x = elements 0,1, ...) to q, which sits
 // d elements past a 16-byte boundary.
@@ -752,12 +749,7 @@ __device__ __forceinline__ uint2 next_lane(uint2 v) {
 template <bool GB>
 __device__ __forceinline__ typename UnitT<GB>::T load_unit(const void *base, int64_t u) {
     if constexpr (GB) {
-        const uint2 *p = reinterpret_cast<const uint2 *>(base) + u;
-        if (ZK_NT_GRAD) {
-            u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
-            return make_uint2(v.x, v.y);
-        }
-        return *p;
+        return ld_u2<ZK_NT_GRAD>(reinterpret_cast<const uint2 *>(base) + u);
     } else {
         return ld_u4<ZK_NT_GRAD>(reinterpret_cast<const uint4 *>(base) + u);
     }
