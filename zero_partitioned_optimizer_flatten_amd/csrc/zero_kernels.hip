@@ -51,6 +51,14 @@ constexpr int kGroup = 8;            // replicas loaded together
 #ifndef ZK_STEP_LDS
 #define ZK_STEP_LDS 22528
 #endif
+// The same for the shifted path, which does more per lane (cross-lane
+// realignment, the last lane's own loads, narrow stores) and measured best
+// with more waves: ten per CU gave 75.5-77.5% of peak HBM bandwidth against
+// 71.9-74.9% at seven, 74.4-75.9% at twelve and 69.4-73.8% at sixteen
+// (7e9-element shard, N = 8, one or seven replicas off the state's phase).
+#ifndef ZK_SHIFT_LDS
+#define ZK_SHIFT_LDS 16384
+#endif
 // Non-temporal (streaming) hints. The replicas are read once and the
 // parameter output written once. For master/m/v the launcher chooses (see
 // StepArgs::stream_state): in the split lane layout of a full wavefront
@@ -1231,7 +1239,7 @@ hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, int tail, hipStr
     const int64_t grid = (nvec + kBlock - 1) / kBlock + (h + tail > 0 ? 1 : 0);
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_shift_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
-                       ZK_STEP_LDS, stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
+                       ZK_SHIFT_LDS, stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
                        nvec, h, tail, a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
