@@ -44,12 +44,13 @@ constexpr int kGroup = 8;            // replicas loaded together
 // cover one contiguous, sliding window of every stream.
 //
 // Dynamic LDS reserved (unused) per fused-step workgroup: caps how many
-// workgroups share a CU (160 KiB of LDS per CU). The default keeps seven
-// one-wave workgroups per CU: measured best (6-8 waves per CU), since more
-// waves put more of the step's 12 streams' requests in flight than the HBM
-// serves well, and fewer leave it idle.
+// workgroups share a CU (160 KiB of LDS per CU). The default keeps six
+// one-wave workgroups per CU: measured best (79.0% of peak HBM bandwidth
+// against 77.9% at seven, 77.3% at eight and 75.4% at ten on the 7e9/N=8
+// shard), since more waves put more of the step's 12 streams' requests in
+// flight than the HBM serves well, and fewer leave it idle.
 #ifndef ZK_STEP_LDS
-#define ZK_STEP_LDS 22528
+#define ZK_STEP_LDS 26624
 #endif
 // The same for the shifted path, which does more per lane (cross-lane
 // realignment, the last lane's own loads, narrow stores) and measured best
@@ -58,6 +59,13 @@ constexpr int kGroup = 8;            // replicas loaded together
 // (7e9-element shard, N = 8, one or seven replicas off the state's phase).
 #ifndef ZK_SHIFT_LDS
 #define ZK_SHIFT_LDS 16384
+#endif
+// The same for the per-parameter step, whose workgroups first search the
+// segment table (dependent scalar loads) before their first vector load:
+// ten per CU gave 78.1% of peak against 76.9% at seven and 73.2% at six;
+// twelve to sixteen 77.7-78.1%, uncapped 77.1% (Llama-7B list, N = 8).
+#ifndef ZK_FSDP_LDS
+#define ZK_FSDP_LDS 16384
 #endif
 // Non-temporal (streaming) hints. The replicas are read once and the
 // parameter output written once. For master/m/v the launcher chooses (see
@@ -1099,7 +1107,7 @@ hipError_t launch_fsdp_typed(const FsdpArgs &a, hipStream_t stream) {
         b.blk0[b.nseg] = blocks;
         if (blocks > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
         hipLaunchKernelGGL((fsdp_step_kernel<NR, EXACT, GB, PB, DS>), dim3((unsigned)blocks),
-                           dim3(kBlock), ZK_STEP_LDS, stream, b, a.n, a.master, a.m, a.v,
+                           dim3(kBlock), ZK_FSDP_LDS, stream, b, a.n, a.master, a.m, a.v,
                            a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
