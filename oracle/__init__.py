@@ -12,10 +12,22 @@ gradients and the parameters" (AI infra handbook), section "Implementing
 ZeRO's Adam from scratch", class ZeroAdam (constructor, _flatten, step,
 state_bytes) and table "The three stages".
 
-Parity pins: every function here is checked in tests/test_oracle_*.py against
-closed forms, the pages' worked example, brute force, invariants or library
-routines (torch.cat, torch.optim.Adam, torch's bf16 cast). Unpinned: the NaN
-payload bits of the bf16 cast (only NaN-ness is compared).
+Parity pins (tests/oracle_pins.py, run by tests/test_oracle_pins.py; each
+planted mistake in tests/test_oracle_mutants.py fails at least one):
+  geometry       brute force over small sizes, exact Fraction ceilings
+  dim0_split     torch.chunk, the page's 128-row FSDP2 example
+  stage_bytes    the page's 13B/16-card worked example, per-component bytes
+  state_bytes    the page's toy model (state_bytes and its 1/4 ratio)
+  flatten        torch.cat plus a zero tail, brute force
+  unflatten      round trip through the pinned flatten
+  bf16_round     torch's bf16 cast over every high half and the tie cases
+  step_scalars   dyadic closed forms; binary64 power rounded once
+  reduce_mean    N = 1, identical replicas, a rank-order example, an error bound
+  shard_step     closed forms, torch.optim.Adam, the page's step lines in torch,
+                 the sharded == unsharded invariant at non-zero offsets
+  load_master    a slice taken at lo (not at 0) of a known vector
+Unpinned: the NaN payload bits of the bf16 cast (only NaN-ness, the sign and
+the quiet bit are compared).
 """
 from __future__ import annotations
 
@@ -64,8 +76,6 @@ def load(path: str):
     L.oracle_bf16_round_array.argtypes = [vp, i64, vp]
     L.oracle_step_scalars.argtypes = [dbl, dbl, dbl, dbl, i64, i32, vp]
     L.oracle_reduce_mean.argtypes = [vp, i32, i32, i64, i64, ctypes.c_float, vp]
-    L.oracle_adam_update.argtypes = [vp, vp, vp, vp, i64, vp]
-    L.oracle_write_params.argtypes = [vp, i64, vp, i32, i64]
     L.oracle_shard_step.argtypes = [vp, i32, i32, i64, vp, vp, vp, i64, vp,
                                     vp, i32, i64]
     L.oracle_load_master.argtypes = [vp, i32, i64, i64, vp, vp, vp]
@@ -205,16 +215,6 @@ def reduce_mean(replicas: Sequence[np.ndarray], offset: int, shard: int,
                                     offset, shard, ctypes.c_float(nf), _ptr(g)),
            "reduce_mean")
     return g
-
-
-def adam_update(g, master, m, v, sc):
-    _check(lib().oracle_adam_update(_ptr(g), _ptr(master), _ptr(m), _ptr(v),
-                                    master.size, _ptr(sc)), "adam_update")
-
-
-def write_params(master, out: np.ndarray, out_offset: int):
-    _check(lib().oracle_write_params(_ptr(master), master.size, _ptr(out),
-                                     _is_bf16(out), out_offset), "write_params")
 
 
 class ShardOracle:

@@ -245,35 +245,10 @@ int oracle_reduce_mean(const void *const *reps, int32_t n, int32_t is_bf16,
     return ORACLE_OK;
 }
 
-/* Adam on the shard, given the averaged gradient.                          */
-int oracle_adam_update(const float *g, float *master, float *m, float *v,
-                       int64_t shard, const float *sc)
-{
-    if (shard < 0 || !sc) return ORACLE_EINVAL;
-    #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < shard; i++)
-        adam_one(g[i], &master[i], &m[i], &v[i], sc);
-    return ORACLE_OK;
-}
-
-/* This rank's contribution to the all-gather: its updated slice written
- * into the flat parameter buffer at `out_off` (bf16 rounded or fp32).      */
-int oracle_write_params(const float *master, int64_t shard, void *out,
-                        int32_t out_bf16, int64_t out_off)
-{
-    if (shard < 0 || !out) return ORACLE_EINVAL;
-    #pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < shard; i++) {
-        if (out_bf16)
-            ((uint16_t *)out)[out_off + i] = oracle_bf16_round(master[i]);
-        else
-            ((float *)out)[out_off + i] = master[i];
-    }
-    return ORACLE_OK;
-}
-
-/* One full shard step: reduce, Adam, write-back; the same per-element
- * functions as above, in one loop (so large shards need no g buffer).     */
+/* One full shard step ([ZF] ZeroAdam.step): reduce, Adam, and this rank's
+ * contribution to the all-gather (its updated slice written into the flat
+ * parameter buffer at `out_off`, bf16 rounded or fp32), element by element
+ * in one loop (so large shards need no g buffer).                          */
 int oracle_shard_step(const void *const *reps, int32_t n, int32_t is_bf16,
                       int64_t grad_off, float *master, float *m, float *v,
                       int64_t shard, const float *sc, void *out,
