@@ -298,7 +298,10 @@ int zero_step_sched(zero_ctx *ctx, const void *const *grad_replicas,
  * one zero_step_begin equals one zero_step_sched. The ranges read the
  * scalars zero_step_begin wrote: a range on another stream must be ordered
  * after that zero_step_begin (e.g. by an event), and must have finished
- * before the next zero_step_begin runs. */
+ * before the next zero_step_begin runs. EINVAL as zero_step_range, and
+ * also while no step has begun on this context's schedule (no
+ * zero_step_begin, zero_step_sched or zero_fsdp_step_sched issued since
+ * zero_schedule_init created it): the scalar block then holds no step. */
 int zero_step_range_sched(zero_ctx *ctx, int64_t shard_begin, int64_t count,
                           const void *const *grad_replicas,
                           int32_t n_replicas, zero_dtype grad_dtype,

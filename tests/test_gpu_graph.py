@@ -73,6 +73,31 @@ def test_scheduled_steps_equal_host_steps():
     st.close()
 
 
+def test_range_step_before_any_begin_is_refused():
+    """A scheduled range step reads the scalars that a begin-step wrote; on
+    a fresh schedule there are none, so the call must fail its argument
+    check and leave the state and the output untouched. After a begin it
+    runs and equals the oracle."""
+    st, orc, reps, out, valid = _setup(10_007, 2, 0, 1e-3)
+    st.schedule(1)
+    _fill(reps, valid, 1)
+    out.fill_(0)
+    before = [x.clone() for x in st.get_state()]
+    with pytest.raises(zero.ZeroError) as ei:
+        st.step_range_sched(0, st.shard, reps, out, grad_offset=0, param_offset=0)
+    assert ei.value.code == zero.ZERO_EINVAL
+    assert "begun" in str(ei.value)
+    torch.cuda.synchronize()
+    after = st.get_state()
+    for a, b in zip(before, after):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert int(out.view(torch.int16).abs().sum()) == 0
+    st.step_begin()
+    st.step_range_sched(0, st.shard, reps, out, grad_offset=0, param_offset=0)
+    _check("range after begin", st, orc, reps, out, 1)
+    st.close()
+
+
 def test_scheduled_steps_past_the_bias_table():
     """Steps far past the point where both bias corrections round to 1
     (the table's end), against the oracle at those t."""

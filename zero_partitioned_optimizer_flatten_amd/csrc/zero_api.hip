@@ -38,6 +38,11 @@ struct zero_ctx {
     zk::StepScalars *sc_dev;
     float *bc_table;             // (1-b1^t, 1-b2^t) for t = 1..bc_len
     int64_t bc_len;
+    // Set once a begin-step kernel has been launched on the schedule: until
+    // then the scalar block holds no step, and a range step that reads it
+    // is refused. Host call order is the launch order on a stream, also
+    // under capture.
+    bool begun;
 };
 
 namespace {
@@ -517,6 +522,7 @@ static int fsdp_step_common(zero_ctx *c, const void *const *grads, int32_t n_rep
     if (mode == kBeginDevice) {
         hipError_t e = begin_device_step(c, stream);
         if (e != hipSuccess) return hip_fail(e, "begin-step launch");
+        c->begun = true;
     }
     if (segs.empty()) return ZERO_OK;
     zk::FsdpArgs a;
@@ -671,6 +677,9 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
         int rc = need_schedule(c);
         if (rc) return rc;
     }
+    if (mode == kCurrentDevice && !c->begun)
+        return fail(ZERO_EINVAL, "no scheduled step has begun: call zero_step_begin (or "
+                                 "zero_step_sched) before a scheduled range step");
     if (!grads) return fail(ZERO_EINVAL, "null replica array");
     if (!param_out) return fail(ZERO_EINVAL, "null parameter output");
     if (!valid_dtype(grad_dtype) || !valid_dtype(param_dtype))
@@ -693,6 +702,7 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
     if (mode == kBeginDevice) {
         hipError_t e = begin_device_step(c, stream);
         if (e != hipSuccess) return hip_fail(e, "begin-step launch");
+        c->begun = true;
     }
     if (count == 0) return ZERO_OK;
 
@@ -753,7 +763,9 @@ int zero_step_begin(zero_ctx *c, hipStream_t stream) {
     DeviceGuard g(c->device);
     if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
     hipError_t e = begin_device_step(c, stream);
-    return e == hipSuccess ? ZERO_OK : hip_fail(e, "begin-step launch");
+    if (e != hipSuccess) return hip_fail(e, "begin-step launch");
+    c->begun = true;
+    return ZERO_OK;
 }
 
 // Bias-correction table: entry t-1 holds (f32(1 - b1^t), f32(1 - b2^t)),
