@@ -35,7 +35,7 @@ namespace {
 #define ZK_BLOCK 64
 #endif
 constexpr int kBlock = ZK_BLOCK;     // fused-step workgroup size (wavefronts of 64 lanes)
-constexpr int kElemBlock = 256;      // element path and master load
+constexpr int kElemBlock = 256;      // element path
 constexpr int kVec = 8;              // elements per lane per vector step
 constexpr int kGroup = 8;            // replicas loaded together
 
@@ -1376,18 +1376,63 @@ __global__ void __launch_bounds__(kCopyBlock) copy_segments_kernel(SegBatch b) {
 }
 
 // ---------------------------------------------------------- master load
-
+// master[i] = fp32(flat[i]), m[i] = v[i] = 0. The launcher starts the vector
+// range at the first element h where master, m and v are 16-byte aligned.
+// A full wavefront block (8 * kBlock elements) takes the split lane layout
+// of the fused step: lane l writes the quads l and l + kBlock, so every
+// store instruction covers one contiguous 1 KiB span of each state array.
+// With SA (the source shares the state's phase: a bf16 quad on 8 bytes, an
+// fp32 quad on 16) a lane reads its quad with one load; otherwise with one
+// load per element (consecutive lanes still read consecutive quads). The
+// h head elements and the tail after the last full block take one extra
+// workgroup, element by element.
 template <bool FB>
-__global__ void __launch_bounds__(kElemBlock)
-load_master_kernel(const void *__restrict__ flat, float *__restrict__ master,
-                   float *__restrict__ mom, float *__restrict__ var, int64_t shard) {
-    const int64_t stride = (int64_t)gridDim.x * kElemBlock;
-    for (int64_t i = (int64_t)blockIdx.x * kElemBlock + threadIdx.x; i < shard; i += stride) {
-        master[i] = FB ? widen_bf16(reinterpret_cast<const uint16_t *>(flat)[i])
-                       : reinterpret_cast<const float *>(flat)[i];
-        mom[i] = 0.0f;
-        var[i] = 0.0f;
+__device__ __forceinline__ float src_elem(const void *flat, int64_t i) {
+    return FB ? widen_bf16(reinterpret_cast<const uint16_t *>(flat)[i])
+              : reinterpret_cast<const float *>(flat)[i];
+}
+
+template <bool FB, bool SA>
+__device__ __forceinline__ float4 src_quad(const void *flat, int64_t e) {
+    if constexpr (SA && FB) {
+        const uint2 w = ld_u2<true>(reinterpret_cast<const uint16_t *>(flat) + e);
+        return make_float4(widen_bf16(w.x & 0xFFFFu), widen_bf16(w.x >> 16),
+                           widen_bf16(w.y & 0xFFFFu), widen_bf16(w.y >> 16));
+    } else if constexpr (SA) {
+        return ld_f4<true>(reinterpret_cast<const float *>(flat) + e);
+    } else {
+        return make_float4(src_elem<FB>(flat, e), src_elem<FB>(flat, e + 1),
+                           src_elem<FB>(flat, e + 2), src_elem<FB>(flat, e + 3));
     }
+}
+
+template <bool FB, bool SA>
+__global__ void __launch_bounds__(kBlock)
+load_master_kernel(const void *__restrict__ flat, float *__restrict__ master,
+                   float *__restrict__ mom, float *__restrict__ var, int64_t shard, int head,
+                   int64_t nblk) {
+    constexpr int64_t per = (int64_t)kVec * kBlock;
+    if ((int64_t)blockIdx.x >= nblk) {                 // head and tail
+        const int64_t t0 = head + nblk * per;
+        const int64_t rest = head + (shard - t0);
+        for (int64_t k = threadIdx.x; k < rest; k += kBlock) {
+            const int64_t i = k < head ? k : t0 + (k - head);
+            master[i] = src_elem<FB>(flat, i);
+            mom[i] = 0.0f;
+            var[i] = 0.0f;
+        }
+        return;
+    }
+    const int64_t e0 = head + (int64_t)blockIdx.x * per + 4 * (int64_t)threadIdx.x;
+    const int64_t e1 = e0 + 4 * kBlock;
+    const float4 a = src_quad<FB, SA>(flat, e0), b = src_quad<FB, SA>(flat, e1);
+    const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+    st_f4<true>(master + e0, a);
+    st_f4<true>(master + e1, b);
+    st_f4<true>(mom + e0, z);
+    st_f4<true>(mom + e1, z);
+    st_f4<true>(var + e0, z);
+    st_f4<true>(var + e1, z);
 }
 
 // ------------------------------------------------------ device step schedule
@@ -1505,14 +1550,36 @@ hipError_t launch_copy_segments(const Segment *segs, int nseg, int esize, hipStr
 hipError_t launch_load_master(const void *flat, bool flat_bf16, float *master, float *m,
                               float *v, int64_t shard, hipStream_t stream) {
     if (shard <= 0) return hipSuccess;
-    int64_t want = (shard + kElemBlock - 1) / kElemBlock;
-    int grid = (int)(want < 65536 ? want : 65536);
-    if (flat_bf16)
-        hipLaunchKernelGGL(load_master_kernel<true>, dim3(grid), dim3(kElemBlock), 0, stream, flat,
-                           master, m, v, shard);
-    else
-        hipLaunchKernelGGL(load_master_kernel<false>, dim3(grid), dim3(kElemBlock), 0, stream, flat,
-                           master, m, v, shard);
+    constexpr int64_t per = (int64_t)kVec * kBlock;
+    // master, m and v share their phase within 16 bytes (the context
+    // allocates them that way); h puts them on a 16-byte boundary
+    int head = (int)(((16u - ((uintptr_t)master & 15u)) & 15u) / 4u);
+    if (((uintptr_t)m & 15u) != ((uintptr_t)master & 15u) ||
+        ((uintptr_t)v & 15u) != ((uintptr_t)master & 15u))
+        return hipErrorInvalidValue;
+    if (head > shard) head = (int)shard;
+    const int64_t nblk = (shard - head) / per;
+    const int64_t grid = nblk + ((shard - nblk * per) > 0 ? 1 : 0);
+    if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
+    const int es = flat_bf16 ? 2 : 4;
+    const uintptr_t src_h = (uintptr_t)flat + (uintptr_t)es * (uintptr_t)head;
+    const bool sa = src_h % (uintptr_t)(4 * es) == 0;
+    const dim3 g((unsigned)grid), blk(kBlock);
+    if (flat_bf16) {
+        if (sa)
+            hipLaunchKernelGGL((load_master_kernel<true, true>), g, blk, 0, stream, flat, master,
+                               m, v, shard, head, nblk);
+        else
+            hipLaunchKernelGGL((load_master_kernel<true, false>), g, blk, 0, stream, flat, master,
+                               m, v, shard, head, nblk);
+    } else {
+        if (sa)
+            hipLaunchKernelGGL((load_master_kernel<false, true>), g, blk, 0, stream, flat, master,
+                               m, v, shard, head, nblk);
+        else
+            hipLaunchKernelGGL((load_master_kernel<false, false>), g, blk, 0, stream, flat, master,
+                               m, v, shard, head, nblk);
+    }
     return hipGetLastError();
 }
 
