@@ -271,6 +271,27 @@ int zero_fsdp_step(zero_ctx *ctx, const void *const *grads, int32_t n_replicas,
  * EINVAL: next_t < 1. EUNSUPPORTED: see ZERO_SCHEDULE_MAX_TABLE. */
 int zero_schedule_init(zero_ctx *ctx, int64_t next_t, hipStream_t stream);
 
+/* zero_schedule_init for callers that cannot allocate device memory
+ * (code under HIP stream capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the schedule lives in a static block of 2 MiB that
+ * the library holds on each device it runs on until the process ends,
+ * instead of an allocation per context. The call allocates nothing and
+ * waits for nothing: it fills the bias-correction table with kernels on
+ * `stream` and sets the next step to next_t and the device lr to the
+ * context's lr, stream-ordered. Scheduled calls then behave exactly as
+ * with zero_schedule_init, bit for bit.
+ * One block per device: a later zero_schedule_init_noalloc by another
+ * context on the same device takes the block over, and this context's
+ * scheduled calls then return EINVAL until it is initialised again (with
+ * either call). Calls that use the block from several streams or contexts
+ * at once race. The block keeps the last call's contents: a scheduled
+ * range step before the first begin-step after this call returns EINVAL.
+ * Limit: the table holds at most 262,080 steps (betas whose 1 - b^t has
+ * not reached 1 in binary32 by then return EUNSUPPORTED; b2 = 0.9999 needs
+ * 180,210). EINVAL: null context, next_t < 1. EHIP: a launch failed. */
+int zero_schedule_init_noalloc(zero_ctx *ctx, int64_t next_t,
+                               hipStream_t stream);
+
 /* Set the learning rate of later scheduled steps (stream-ordered; also the
  * context's host lr). A captured graph takes the lr the device holds when
  * it replays. EINVAL: no schedule, lr not finite. */

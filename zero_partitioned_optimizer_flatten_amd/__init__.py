@@ -69,6 +69,7 @@ def lib():
     L.zero_fsdp_load_master.argtypes = [vp, vp, ctypes.c_int, vp]
     L.zero_fsdp_step.argtypes = [vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, i64, vp]
     L.zero_schedule_init.argtypes = [vp, i64, vp]
+    L.zero_schedule_init_noalloc.argtypes = [vp, i64, vp]
     L.zero_schedule_lr.argtypes = [vp, dbl, vp]
     L.zero_schedule_get.argtypes = [vp, p64, vp]
     L.zero_step_begin.argtypes = [vp, vp]
@@ -302,6 +303,13 @@ class ShardState:
         outside any graph capture): the next scheduled step is next_t."""
         with torch.cuda.device(self.device):
             _check(lib().zero_schedule_init(self._h, int(next_t), _stream_handle(stream)))
+
+    def schedule_noalloc(self, next_t: int = 1, stream=None):
+        """schedule() in the device's static block: allocates nothing (one
+        such schedule per device at a time)."""
+        with torch.cuda.device(self.device):
+            _check(lib().zero_schedule_init_noalloc(self._h, int(next_t),
+                                                    _stream_handle(stream)))
 
     def schedule_lr(self, lr: float, stream=None):
         """Learning rate of later scheduled steps (stream-ordered)."""

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -31,9 +32,14 @@ struct zero_ctx {
     int num_cus;
     void *state;                 // one allocation: master | m | v
     float *master, *m, *v;
-    // device-resident step schedule (zero_schedule_init), one allocation:
-    // schedule | scalars of the current step | bias-correction table
+    // device-resident step schedule, one block: schedule | scalars of the
+    // current step | bias-correction table. It is either the context's own
+    // allocation (zero_schedule_init: sched_mem, sched_mem_len) or the
+    // device's static block (zero_schedule_init_noalloc: sched_static);
+    // ds, sc_dev, bc_table and bc_len describe the one in use.
     void *sched_mem;
+    int64_t sched_mem_len;
+    bool sched_static;
     zk::DevSchedule *ds;
     zk::StepScalars *sc_dev;
     float *bc_table;             // (1-b1^t, 1-b2^t) for t = 1..bc_len
@@ -44,6 +50,14 @@ struct zero_ctx {
     // under capture.
     bool begun;
 };
+
+// The static schedule block of zero_schedule_init_noalloc: one per device
+// that loads the library, held until the process ends. Host code never
+// uses the array's name as an address (in host code it is a stand-in, not
+// device memory): the device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is used.
+constexpr size_t kScratchBytes = (size_t)2 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -181,9 +195,51 @@ enum StepMode {
     kCurrentDevice = 2,  // the scalars of the schedule's current step
 };
 
+// Layout of a schedule block: DevSchedule at 0, the current step's scalars
+// at 256, the bias-correction table from 512.
+constexpr size_t kSchedHead = 512;
+constexpr size_t kSchedScalars = 256;
+
+constexpr int64_t kScratchMaxTable = (int64_t)((kScratchBytes - kSchedHead) / (2 * sizeof(float)));
+constexpr int kMaxDevices = 256;
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];              // device address of `scratch`, per device
+const zero_ctx *g_scratch_owner[kMaxDevices];  // context whose schedule it holds
+
+// Resolve the static block's address on the current device `dev` (once).
+int scratch_address(int dev, void **out) {
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ZERO_EUNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return fail(ZERO_EHIP, "hipGetSymbolAddress of the static schedule block: %s",
+                        hipGetErrorString(e));
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ZERO_OK;
+}
+
+bool owns_scratch(const zero_ctx *c) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    return c->device >= 0 && c->device < kMaxDevices && g_scratch_owner[c->device] == c;
+}
+
 int need_schedule(const zero_ctx *c) {
-    if (!c->sched_mem)
-        return fail(ZERO_EINVAL, "no device step schedule: call zero_schedule_init first");
+    if (!c->ds)
+        return fail(ZERO_EINVAL, "no device step schedule: call zero_schedule_init (or "
+                                 "zero_schedule_init_noalloc) first");
+    if (c->sched_static && !owns_scratch(c))
+        return fail(ZERO_EINVAL, "this context's static step schedule was taken over by "
+                                 "another context on the same device "
+                                 "(zero_schedule_init_noalloc); initialise it again");
     return ZERO_OK;
 }
 
@@ -302,6 +358,14 @@ static int alloc_state(zero_ctx *c, int shift) {
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
     c->device = dev;
     c->num_cus = cus > 0 ? cus : 256;
+    // the static schedule block's address on this device, resolved at set-up
+    // so that zero_schedule_init_noalloc makes no runtime query later; a
+    // failure here only matters to that call, which resolves it again and
+    // reports it
+    if (dev >= 0 && dev < kMaxDevices) {
+        void *unused = nullptr;
+        if (scratch_address(dev, &unused) != ZERO_OK) g_last_error.clear();
+    }
     // master | m | v, each segment a whole number of kStateAlign blocks plus
     // kStateStagger, the first starting on a kStateAlign boundary inside the
     // allocation
@@ -772,14 +836,25 @@ int zero_step_begin(zero_ctx *c, hipStream_t stream) {
 // formed exactly as for a host step count. It ends at the first t where
 // both b^t < 2^-26: from there on 1 - b^t rounds to 1 in binary32 for every
 // later t, and the last entry is (1, 1).
-static int bias_table(const zero_ctx *c, std::vector<float> &tab) {
+static int bias_table_len(const zero_ctx *c, int64_t cap, int64_t *len_out) {
     const double tiny = std::ldexp(1.0, -26);
     int64_t len = 1;
     while (std::pow(c->beta1, (double)len) >= tiny || std::pow(c->beta2, (double)len) >= tiny) {
-        if (++len > ZERO_SCHEDULE_MAX_TABLE)
+        if (++len > cap)
             return fail(ZERO_EUNSUPPORTED, "betas (%g, %g) need a bias-correction table of more "
-                        "than %d steps", c->beta1, c->beta2, ZERO_SCHEDULE_MAX_TABLE);
+                        "than %lld steps", c->beta1, c->beta2, (long long)cap);
     }
+    const zk::StepScalars last = make_scalars(c, len);
+    if (last.bc1 != 1.0f || last.bc2 != 1.0f)
+        return fail(ZERO_EHIP, "bias-correction table does not end at (1, 1)");
+    *len_out = len;
+    return ZERO_OK;
+}
+
+static int bias_table(const zero_ctx *c, std::vector<float> &tab) {
+    int64_t len = 0;
+    int rc = bias_table_len(c, ZERO_SCHEDULE_MAX_TABLE, &len);
+    if (rc) return rc;
     try {
         tab.resize((size_t)(2 * len));
     } catch (...) {
@@ -790,9 +865,16 @@ static int bias_table(const zero_ctx *c, std::vector<float> &tab) {
         tab[(size_t)(2 * (t - 1))] = sc.bc1;
         tab[(size_t)(2 * (t - 1) + 1)] = sc.bc2;
     }
-    if (tab[(size_t)(2 * len - 2)] != 1.0f || tab[(size_t)(2 * len - 1)] != 1.0f)
-        return fail(ZERO_EHIP, "bias-correction table does not end at (1, 1)");
     return ZERO_OK;
+}
+
+// Point the context's schedule at a block (its own or the static one).
+static void use_schedule_block(zero_ctx *c, void *mem, int64_t len, bool is_static) {
+    c->ds = (zk::DevSchedule *)mem;
+    c->sc_dev = (zk::StepScalars *)((char *)mem + kSchedScalars);
+    c->bc_table = (float *)((char *)mem + kSchedHead);
+    c->bc_len = len;
+    c->sched_static = is_static;
 }
 
 int zero_schedule_init(zero_ctx *c, int64_t next_t, hipStream_t stream) {
@@ -804,26 +886,71 @@ int zero_schedule_init(zero_ctx *c, int64_t next_t, hipStream_t stream) {
         std::vector<float> tab;
         int rc = bias_table(c, tab);
         if (rc) return rc;
-        const size_t head = 512, bytes = head + tab.size() * sizeof(float);
+        const size_t bytes = kSchedHead + tab.size() * sizeof(float);
         void *mem = nullptr;
         hipError_t e = hipMalloc(&mem, bytes);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(ZERO_ENOMEM, "hipMalloc of %zu bytes for the step schedule failed", bytes);
         }
-        e = hipMemset(mem, 0, head);
+        e = hipMemset(mem, 0, kSchedHead);
         if (e == hipSuccess)
-            e = hipMemcpy((char *)mem + head, tab.data(), tab.size() * sizeof(float),
+            e = hipMemcpy((char *)mem + kSchedHead, tab.data(), tab.size() * sizeof(float),
                           hipMemcpyHostToDevice);
         if (e != hipSuccess) {
             (void)hipFree(mem);
             return hip_fail(e, "uploading the step schedule");
         }
         c->sched_mem = mem;
-        c->ds = (zk::DevSchedule *)mem;
-        c->sc_dev = (zk::StepScalars *)((char *)mem + 256);
-        c->bc_table = (float *)((char *)mem + head);
-        c->bc_len = (int64_t)(tab.size() / 2);
+        c->sched_mem_len = (int64_t)(tab.size() / 2);
+    }
+    if (c->ds != (zk::DevSchedule *)c->sched_mem) {
+        use_schedule_block(c, c->sched_mem, c->sched_mem_len, false);
+        c->begun = false;    // this block's scalars were resolved for no step of ours
+    }
+    hipError_t e = zk::launch_set_schedule(c->ds, next_t, (float)c->lr, stream);
+    return e == hipSuccess ? ZERO_OK : hip_fail(e, "schedule launch");
+}
+
+int zero_schedule_init_noalloc(zero_ctx *c, int64_t next_t, hipStream_t stream) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (next_t < 1) return fail(ZERO_EINVAL, "next step must be >= 1 (got %lld)", (long long)next_t);
+    int64_t len = 0;
+    int rc = bias_table_len(c, kScratchMaxTable, &len);
+    if (rc == ZERO_EUNSUPPORTED)
+        return fail(ZERO_EUNSUPPORTED, "betas (%g, %g) need a bias-correction table longer than "
+                    "the %lld steps the static schedule block (%zu bytes) holds; use "
+                    "zero_schedule_init", c->beta1, c->beta2, (long long)kScratchMaxTable,
+                    kScratchBytes);
+    if (rc) return rc;
+    DeviceGuard g(c->device);
+    if (g.error() != hipSuccess) return hip_fail(g.error(), "hipSetDevice");
+    void *base = nullptr;
+    rc = scratch_address(c->device, &base);
+    if (rc) return rc;
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        g_scratch_owner[c->device] = c;
+    }
+    use_schedule_block(c, base, len, true);
+    c->begun = false;        // the block holds whatever the last call left there
+    // the table, entry t-1 = (f32(1 - b1^t), f32(1 - b2^t)), in chunks carried
+    // by the fill kernel's arguments
+    zk::WordChunk chunk;
+    uint32_t *dst = reinterpret_cast<uint32_t *>(c->bc_table);
+    int64_t done = 0;                        // words issued
+    const int64_t words = 2 * len;
+    static_assert(zk::kWordChunk % 2 == 0, "whole table entries per chunk");
+    while (done < words) {
+        chunk.n = (int)(words - done < zk::kWordChunk ? words - done : zk::kWordChunk);
+        for (int k = 0; k < chunk.n; k += 2) {
+            const zk::StepScalars sc = make_scalars(c, (done + k) / 2 + 1);
+            std::memcpy(&chunk.w[k], &sc.bc1, sizeof(float));
+            std::memcpy(&chunk.w[k + 1], &sc.bc2, sizeof(float));
+        }
+        hipError_t e = zk::launch_fill_words(dst + done, chunk, stream);
+        if (e != hipSuccess) return hip_fail(e, "uploading the static step schedule");
+        done += chunk.n;
     }
     hipError_t e = zk::launch_set_schedule(c->ds, next_t, (float)c->lr, stream);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "schedule launch");
@@ -894,6 +1021,11 @@ void zero_destroy(zero_ctx *c) {
     (void)hipDeviceSynchronize();
     if (c->state) (void)hipFree(c->state);
     if (c->sched_mem) (void)hipFree(c->sched_mem);
+    {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        if (c->device >= 0 && c->device < kMaxDevices && g_scratch_owner[c->device] == c)
+            g_scratch_owner[c->device] = nullptr;
+    }
     delete c;
 }
 

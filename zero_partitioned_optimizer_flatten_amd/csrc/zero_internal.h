@@ -61,6 +61,17 @@ hipError_t launch_begin_step(DevSchedule *ds, const float *table, int64_t len,
 // ds->t = t (if t >= 1) and ds->lr = lr, stream-ordered.
 hipError_t launch_set_schedule(DevSchedule *ds, int64_t t, float lr, hipStream_t stream);
 
+// Up to kWordChunk 32-bit words carried in the kernel arguments (which
+// stay under 4 KiB) and stored at dst, stream-ordered: fills device memory
+// from the host without a copy call or a staging buffer.
+constexpr int kWordChunk = 1000;
+struct WordChunk {
+    uint32_t w[kWordChunk];
+    int n;
+};
+static_assert(sizeof(WordChunk) <= 4096, "word chunk must fit the kernel arguments");
+hipError_t launch_fill_words(uint32_t *dst, const WordChunk &c, hipStream_t stream);
+
 // Per-parameter (dim-0) layout: one segment per parameter's local shard.
 constexpr int kFsdpMaxWorld = 16;
 struct FsdpSegment {

@@ -1454,6 +1454,12 @@ begin_step_kernel(DevSchedule *ds, const float *__restrict__ table, int64_t len,
     ds->t = t + 1;
 }
 
+// dst[i] = c.w[i] for i < c.n: words passed by value in the kernel
+// arguments, so a host table reaches device memory without a copy call.
+__global__ void __launch_bounds__(256) fill_words_kernel(uint32_t *dst, WordChunk c) {
+    for (int i = threadIdx.x; i < c.n; i += 256) dst[i] = c.w[i];
+}
+
 __global__ void __launch_bounds__(64)
 set_schedule_kernel(DevSchedule *ds, int64_t t, float lr) {
     if (threadIdx.x != 0) return;
@@ -1466,6 +1472,13 @@ set_schedule_kernel(DevSchedule *ds, int64_t t, float lr) {
 hipError_t launch_begin_step(DevSchedule *ds, const float *table, int64_t len,
                              const StepScalars &base, StepScalars *out, hipStream_t stream) {
     hipLaunchKernelGGL(begin_step_kernel, dim3(1), dim3(64), 0, stream, ds, table, len, base, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_words(uint32_t *dst, const WordChunk &c, hipStream_t stream) {
+    if (c.n < 0 || c.n > kWordChunk) return hipErrorInvalidValue;
+    if (c.n == 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_words_kernel, dim3(1), dim3(256), 0, stream, dst, c);
     return hipGetLastError();
 }
 
