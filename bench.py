@@ -24,7 +24,8 @@ shifted path) and at the phase they have inside full flat buffers.
 
 The default workload also times extras, each selectable with `--extras`:
 the bucketed step eager on 2 streams (buckets), replayed from a HIP graph
-(graph), beside bf16 GEMMs (gemm), the Llama-7B tensor-list flatten and
+(graph), beside bf16 GEMMs with and without a workgroup cap (gemm) and on
+CU-partitioned streams (partition), the Llama-7B tensor-list flatten and
 unflatten (lists), and the per-parameter dim-0 layout step (fsdp).
 """
 from __future__ import annotations
@@ -227,10 +228,12 @@ def bucketed_graph_extras(st, reps, out, t0, sizes=(1 << 20, 1 << 22, 1 << 24),
     return res
 
 
-def overlap_extras(st, reps, out, t0, bucket=1 << 26, n=4096, gemms=12):
+def overlap_extras(st, reps, out, t0, bucket=1 << 26, n=4096, gemms=48, caps=(0, 1, 2, 4)):
     """Why buckets: the step is HBM-bound, a backward pass mostly MFMA-bound.
-    bf16 GEMMs (n x n x n) on one stream and the bucketed step on another,
-    timed alone and together."""
+    bf16 GEMMs (n x n x n, about as long in all as the step) on one stream
+    and the bucketed step on another, timed alone and together, with the
+    step's workgroups uncapped (cap 0) and capped at `cap` per compute unit
+    (zero_set_step_workgroups)."""
     S = st.shard
     a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
     b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
@@ -239,32 +242,168 @@ def overlap_extras(st, reps, out, t0, bucket=1 << 26, n=4096, gemms=12):
     cur = torch.cuda.current_stream()
     t = [t0]
 
-    def run_gemms():
-        gs.wait_stream(cur)
+    def launch_gemms():
         with torch.cuda.stream(gs):
             for _ in range(gemms):
                 torch.matmul(a, b, out=c)
+
+    def launch_steps():
+        for b0 in range(0, S, bucket):
+            st.step_range(b0, min(bucket, S - b0), reps, t[0], out, grad_offset=b0,
+                          param_offset=b0, stream=ss)
+        t[0] += 1
+
+    def run_gemms():
+        gs.wait_stream(cur)
+        launch_gemms()
         cur.wait_stream(gs)
 
     def run_steps():
         ss.wait_stream(cur)
+        launch_steps()
+        cur.wait_stream(ss)
+
+    def both():
+        # both side streams start after the current stream's work; the
+        # current stream then waits for both (no order between the two)
+        gs.wait_stream(cur)
+        ss.wait_stream(cur)
+        launch_gemms()
+        launch_steps()
+        cur.wait_stream(gs)
+        cur.wait_stream(ss)
+
+    ms_g = _time_ms(run_gemms, reps=3)
+    res = {"gemm": {"n": n, "count": gemms, "ms": ms_g,
+                    "tflops": 2.0 * n ** 3 * gemms / (ms_g * 1e-3) / 1e12},
+           "bucket": bucket, "by_cap": {}}
+    for cap in caps:
+        st.set_step_workgroups(cap)
+        ms_s = _time_ms(run_steps, reps=3)
+        ms_b = _time_ms(both, reps=3)
+        res["by_cap"][str(cap)] = {
+            "bucketed_step_ms": ms_s, "together_ms": ms_b,
+            "step_gbps": step_bytes_per_elem(WORLD) * S / (ms_s * 1e-3) / 1e9,
+            "hidden_fraction_of_step": (ms_g + ms_s - ms_b) / ms_s}
+    st.set_step_workgroups(0)
+    del a, b, c
+    return res
+
+
+_HIP = None
+
+
+def _hip_runtime():
+    """The HIP runtime library this process already loaded (through torch),
+    for the stream calls torch does not expose."""
+    global _HIP
+    if _HIP is None:
+        import ctypes
+        path = None
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64.so" in line:
+                    path = line.split()[-1]
+                    break
+        if path is None:
+            raise RuntimeError("HIP runtime not loaded")
+        L = ctypes.CDLL(path)
+        L.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                   ctypes.c_uint32,
+                                                   ctypes.POINTER(ctypes.c_uint32)]
+        L.hipStreamDestroy.argtypes = [ctypes.c_void_p]
+        _HIP = L
+    return _HIP
+
+
+def cu_partition(n_cus, share):
+    """Two CU masks: share/8 of the CUs for the first, the rest for the
+    second, such that each of the 8 XCDs holds share/8 of its CUs in the
+    first whether mask bit c belongs to XCD c // (n_cus / 8) or to XCD c % 8."""
+    per = n_cus // 8
+    pick = [((c % 8) + c // per) % 8 < share for c in range(n_cus)]
+    return ([c for c in range(n_cus) if pick[c]], [c for c in range(n_cus) if not pick[c]])
+
+
+def cu_masked_stream(cus, n_cus):
+    """A default-priority stream whose kernels run only on the listed CUs."""
+    import ctypes
+    words = (n_cus + 31) // 32
+    mask = (ctypes.c_uint32 * words)()
+    for c in cus:
+        mask[c // 32] |= 1 << (c % 32)
+    h = ctypes.c_void_p()
+    rc = _hip_runtime().hipExtStreamCreateWithCUMask(ctypes.byref(h), words, mask)
+    if rc != 0:
+        raise RuntimeError(f"hipExtStreamCreateWithCUMask failed ({rc})")
+    return torch.cuda.ExternalStream(h.value), h
+
+
+def partition_extras(st, reps, out, t0, bucket=1 << 26, n=4096, gemms=48,
+                     shares=((1, 2), (2, 0), (2, 4), (4, 4), (4, 8))):
+    """The bucketed step and bf16 GEMMs on CU-partitioned streams: the step
+    on share/8 of the CUs (capped at `cap` workgroups per device CU, all of
+    which land on its share), the GEMMs on the rest. Against the two run
+    one after the other on the whole device."""
+    S = st.shard
+    n_cus = torch.cuda.get_device_properties(0).multi_processor_count
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device="cuda")
+    cur = torch.cuda.current_stream()
+    t = [t0]
+
+    def launch_gemms(gs):
+        with torch.cuda.stream(gs):
+            for _ in range(gemms):
+                torch.matmul(a, b, out=c)
+
+    def launch_steps(ss):
         for b0 in range(0, S, bucket):
             st.step_range(b0, min(bucket, S - b0), reps, t[0], out, grad_offset=b0,
                           param_offset=b0, stream=ss)
-        cur.wait_stream(ss)
         t[0] += 1
 
-    def both():
-        run_gemms()
-        run_steps()
+    def on(launch, *streams):
+        # the side streams start after the current stream's work, and the
+        # current stream waits for all of them (no order among them)
+        def run():
+            for x in streams:
+                x.wait_stream(cur)
+            launch()
+            for x in streams:
+                cur.wait_stream(x)
+        return run
 
-    ms_g = _time_ms(run_gemms, reps=3)
-    ms_s = _time_ms(run_steps, reps=3)
-    ms_b = _time_ms(both, reps=3)
-    tflops = 2.0 * n ** 3 * gemms / (ms_g * 1e-3) / 1e12
-    res = {"gemm": {"n": n, "count": gemms, "ms": ms_g, "tflops": tflops},
-           "bucketed_step_ms": ms_s, "together_ms": ms_b,
-           "hidden_fraction_of_step": (ms_g + ms_s - ms_b) / ms_s}
+    def gemm_on(gs):
+        return on(lambda: launch_gemms(gs), gs)
+
+    def step_on(ss):
+        return on(lambda: launch_steps(ss), ss)
+
+    whole_g, whole_s = torch.cuda.Stream(), torch.cuda.Stream()
+    ms_g = _time_ms(gemm_on(whole_g), reps=3)
+    st.set_step_workgroups(0)
+    ms_s = _time_ms(step_on(whole_s), reps=3)
+    ms_b = _time_ms(on(lambda: (launch_gemms(whole_g), launch_steps(whole_s)), whole_g,
+                       whole_s), reps=3)
+    res = {"gemm_ms": ms_g, "step_ms": ms_s, "serial_ms": ms_g + ms_s, "n_cus": n_cus,
+           "unpartitioned_together_ms": ms_b, "by_partition": {}}
+    for share, cap in shares:
+        sc, gc = cu_partition(n_cus, share)
+        ss, sh = cu_masked_stream(sc, n_cus)
+        gs, gh = cu_masked_stream(gc, n_cus)
+        st.set_step_workgroups(cap)
+        ms_ps = _time_ms(step_on(ss), reps=3)
+        ms_pg = _time_ms(gemm_on(gs), reps=3)
+        ms_b = _time_ms(on(lambda: (launch_gemms(gs), launch_steps(ss)), gs, ss), reps=3)
+        torch.cuda.synchronize()
+        _hip_runtime().hipStreamDestroy(sh)
+        _hip_runtime().hipStreamDestroy(gh)
+        res["by_partition"][f"step_cus={len(sc)},cap={cap}"] = {
+            "step_alone_ms": ms_ps, "gemm_alone_ms": ms_pg, "together_ms": ms_b,
+            "hidden_fraction_of_step": (ms_g + ms_s - ms_b) / ms_s}
+    st.set_step_workgroups(0)
     del a, b, c
     return res
 
@@ -337,24 +476,24 @@ def fsdp_extras(dev, steps=5):
 
 
 def copy_ceiling(nbytes: int, reps: int = 5):
-    """torch device-to-device copy as a plain-copy context figure."""
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    del a, b
+    """Plain-copy context figures: the library's own copy kernel (the flatten
+    of one bf16 tensor of nbytes, no pad: a plain copy of known size) and
+    torch's device-to-device copy, in GB/s counting bytes read + written."""
+    numel = nbytes // 2
+    st = zero.ShardState(numel, 1, 0, LR, BETAS, EPS)
+    src = torch.empty(numel, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty(numel, dtype=torch.bfloat16, device="cuda")
+    src.view(torch.int16).random_(-30000, 30000)
+    ms_lib = _time_ms(lambda: st.flatten([src], dst), reps=reps)
+    assert torch.equal(src.view(torch.int16), dst.view(torch.int16))
+    ms_torch = _time_ms(lambda: dst.copy_(src), reps=reps)
+    st.close()
+    del src, dst
     torch.cuda.empty_cache()
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+    return (2 * numel * 2 / (ms_lib * 1e-3) / 1e9, 2 * numel * 2 / (ms_torch * 1e-3) / 1e9)
 
 
-EXTRAS = ("buckets", "graph", "gemm", "lists", "fsdp")
+EXTRAS = ("buckets", "graph", "gemm", "partition", "lists", "fsdp")
 
 WORKLOADS = {
     "flat7b_n8_rank0": dict(
@@ -559,6 +698,9 @@ def main():
     if "gemm" in chosen:
         log("bucketed step beside bf16 GEMMs")
         extras["bucketed_step_beside_gemm"] = overlap_extras(st, reps, out, n_total + 200)
+    if "partition" in chosen:
+        log("bucketed step and bf16 GEMMs on CU-partitioned streams")
+        extras["bucketed_step_cu_partition"] = partition_extras(st, reps, out, n_total + 300)
 
     del inp, reps, out, own_tensors, own_flat
     st.close()
@@ -566,10 +708,13 @@ def main():
 
     context = {}
     if not args.no_context:
-        context["torch_copy_gbps"] = round(copy_ceiling(8 << 30), 1)
-        context["note"] = "torch's own device-to-device copy of 8 GiB" + (
-            "; the one-tensor flatten in kernels.flatten is a plain copy through the library"
-            if k1_bytes and ntensors == 1 else "")
+        lib_gbps, torch_gbps = copy_ceiling(8 << 30)
+        context["plain_copy_gbps"] = round(lib_gbps, 1)
+        context["plain_copy_frac_of_peak"] = round(lib_gbps / PEAK_HBM_GBPS, 4)
+        context["torch_copy_gbps"] = round(torch_gbps, 1)
+        context["note"] = ("plain_copy: the library's copy kernel on one 8 GiB bf16 tensor "
+                           "(read + written bytes), the achievable-bandwidth ceiling for a "
+                           "2-stream copy; torch_copy: torch's own device copy of the same")
     if "lists" in chosen:
         log("tensor-list flatten/unflatten")
         extras["llama7b_list"] = list_extras(dev)

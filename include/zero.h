@@ -189,6 +189,18 @@ int zero_step_range(zero_ctx *ctx, int64_t shard_begin, int64_t count,
                     void *param_out, zero_dtype param_dtype,
                     int64_t param_offset, int64_t t, hipStream_t stream);
 
+/* Cap the workgroups of later flat-layout steps (zero_step,
+ * zero_step_range and their scheduled forms) at per_cu times the device's
+ * compute units; 0 (the default) removes the cap. Uncapped, the fused step
+ * makes one pass over its range with one workgroup per 512-element block
+ * and fills every compute unit, so kernels on other streams (a backward
+ * pass's GEMMs next to gradient buckets, [ZeRO and FSDP], the note after
+ * the 4-process test) only start as it drains. Capped, each workgroup walks
+ * blocks at a stride of the cap, leaving room on every compute unit; the
+ * results are bit-identical (the update is elementwise). Host only; EINVAL
+ * unless 0 <= per_cu <= 64. */
+int zero_set_step_workgroups(zero_ctx *ctx, int32_t per_cu);
+
 /* ---- Per-parameter (dim-0) layout ------------------------------------
  * [ZeRO and FSDP], section "ZeRO-3 and FSDP": FSDP2 keeps every parameter
  * as a tensor partitioned along dimension 0, and the optimizer acts on the

@@ -44,4 +44,4 @@ def test_unknown_extras_are_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--extras", "fsdp,nope"],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "unknown extras: nope" in r.stderr
-    assert set(bench.EXTRAS) == {"buckets", "graph", "gemm", "lists", "fsdp"}
+    assert set(bench.EXTRAS) == {"buckets", "graph", "gemm", "partition", "lists", "fsdp"}

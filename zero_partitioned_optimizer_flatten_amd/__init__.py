@@ -68,6 +68,7 @@ def lib():
     L.zero_fsdp_local.argtypes = [vp, i32, p64, p64, p64]
     L.zero_fsdp_load_master.argtypes = [vp, vp, ctypes.c_int, vp]
     L.zero_fsdp_step.argtypes = [vp, vp, i32, ctypes.c_int, vp, ctypes.c_int, i64, vp]
+    L.zero_set_step_workgroups.argtypes = [vp, i32]
     L.zero_schedule_init.argtypes = [vp, i64, vp]
     L.zero_schedule_init_noalloc.argtypes = [vp, i64, vp]
     L.zero_schedule_lr.argtypes = [vp, dbl, vp]
@@ -178,6 +179,11 @@ class ShardState:
         self.close()
 
     # ------------------------------------------------------------- calls
+    def set_step_workgroups(self, per_cu: int):
+        """Cap later flat-layout steps at per_cu workgroups per compute unit
+        (0: uncapped); results are unchanged."""
+        _check(lib().zero_set_step_workgroups(self._h, int(per_cu)))
+
     def set_lr(self, lr: float):
         _check(lib().zero_set_lr(self._h, float(lr)))
 

@@ -30,6 +30,7 @@ struct zero_ctx {
     double lr, beta1, beta2, eps;
     int device;
     int num_cus;
+    int32_t step_wgs_per_cu;     // zero_set_step_workgroups (0: no cap)
     void *state;                 // one allocation: master | m | v
     float *master, *m, *v;
     // device-resident step schedule, one block: schedule | scalars of the
@@ -634,6 +635,14 @@ int zero_set_lr(zero_ctx *c, double lr) {
     return ZERO_OK;
 }
 
+int zero_set_step_workgroups(zero_ctx *c, int32_t per_cu) {
+    if (!c) return fail(ZERO_EINVAL, "null context");
+    if (per_cu < 0 || per_cu > 64)
+        return fail(ZERO_EINVAL, "workgroups per compute unit must be in [0, 64] (got %d)", per_cu);
+    c->step_wgs_per_cu = per_cu;
+    return ZERO_OK;
+}
+
 int zero_load_master(zero_ctx *c, const void *flat, zero_dtype dtype, int64_t flat_offset,
                      hipStream_t stream) {
     if (!c) return fail(ZERO_EINVAL, "null context");
@@ -770,7 +779,7 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
     }
     if (count == 0) return ZERO_OK;
 
-    zk::StepArgs a;
+    zk::StepArgs a = {};
     a.grads = slices;
     a.n = n_replicas;
     a.grad_bf16 = grad_dtype == ZERO_BF16;
@@ -784,6 +793,7 @@ static int step_common(zero_ctx *c, int64_t begin, int64_t count, const void *co
     a.sc_dev = mode == kHostT ? nullptr : c->sc_dev;
     a.num_cus = c->num_cus;
     a.stream_state = zk::state_streams(c->shard);
+    a.max_workgroups = (int64_t)c->step_wgs_per_cu * c->num_cus;
     hipError_t e = zk::launch_step(a, stream);
     return e == hipSuccess ? ZERO_OK : hip_fail(e, "step launch");
 }

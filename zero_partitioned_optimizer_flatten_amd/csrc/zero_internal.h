@@ -45,6 +45,11 @@ struct StepArgs {
     // context's whole state, not just this launch's range, is larger than
     // the Infinity Cache: it cannot stay cached from one step to the next.
     bool stream_state;
+    // Cap on the workgroups that take the vector path's full blocks (0: one
+    // per block, a single pass). A capped launch leaves room on every CU
+    // for work on other streams; each workgroup then walks the blocks at a
+    // stride of the cap, with the same per-element arithmetic.
+    int64_t max_workgroups;
 };
 // MI355X's last-level (Infinity) cache in front of HBM.
 constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;

@@ -463,38 +463,45 @@ __device__ __forceinline__ const void *rep_base(const Reps<NR> &r, int q, int) {
 // the split lane layout; the last, partial block has lane j - 64*block
 // handle elements [8j, 8j+8) of vector j. NR > 0 fixes the replica count at compile time
 // (N <= 16 fully unrolled; larger N walks the groups in a loop to bound
-// register use); NR == 0 reads it from `nrep`. One workgroup past the
-// vector range, launched when head + tail > 0, steps the `head` elements
-// just before element 0 and the `tail` elements after the last vector one
-// by one, so a shard takes one launch whatever its alignment.
+// register use); NR == 0 reads it from `nrep`. Workgroups [0, nbw) take
+// the full blocks: block w, then w + nbw, ... (nbw = the number of full
+// blocks unless the launch is capped, so normally one block each, one pass
+// over the shard). The next workgroup takes the partial block, if any, and
+// one more, launched when head + tail > 0, steps the `head` elements just
+// before element 0 and the `tail` elements after the last vector one by
+// one, so a shard takes one launch whatever its alignment.
 template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
                 float *__restrict__ mom, float *__restrict__ var,
-                void *__restrict__ out, int64_t nvec, int head, int tail, int nt_state,
-                ScalarArg<DS> sa) {
+                void *__restrict__ out, int64_t nvec, int64_t nbw, int head, int tail,
+                int nt_state, ScalarArg<DS> sa) {
     const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
-    if ((int64_t)blockIdx.x * kBlock >= nvec) {
-        for (int k = threadIdx.x; k < head + tail; k += kBlock) {
-            const int64_t e = k < head ? (int64_t)(k - head) : nvec * kVec + (k - head);
-            step_one<NR, GB, PB>(reps, n, master, mom, var, out, e, sc);
+    constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
+    const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
+    const int64_t nfull = nvec / kBlock;
+    const int64_t w = blockIdx.x;
+    if (w < nbw) {
+        for (int64_t blk = w; blk < nfull; blk += nbw) {
+            const int64_t q0 = blk * 2 * kBlock + threadIdx.x;
+            if (nt_state)
+                step_vector_split<NR, GB, PB, true>(reps, n, pow2, master, mom, var, out, q0, sc);
+            else
+                step_vector_split<NR, GB, PB, false>(reps, n, pow2, master, mom, var, out, q0,
+                                                     sc);
         }
         return;
     }
-    constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
-    const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
-    const int64_t vb = blockIdx.x;
-    if ((vb + 1) * kBlock <= nvec) {
-        const int64_t q0 = vb * 2 * kBlock + threadIdx.x;
-        if (nt_state)
-            step_vector_split<NR, GB, PB, true>(reps, n, pow2, master, mom, var, out, q0, sc);
-        else
-            step_vector_split<NR, GB, PB, false>(reps, n, pow2, master, mom, var, out, q0, sc);
+    if (w == nbw && nfull * kBlock < nvec) {
+        const int64_t j = nfull * kBlock + threadIdx.x;
+        if (j < nvec) step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
         return;
     }
-    const int64_t j = vb * kBlock + threadIdx.x;
-    if (j < nvec) step_vector<NR, GB, PB>(reps, n, pow2, master, mom, var, out, j, sc);
+    for (int k = threadIdx.x; k < head + tail; k += kBlock) {
+        const int64_t e = k < head ? (int64_t)(k - head) : nvec * kVec + (k - head);
+        step_one<NR, GB, PB>(reps, n, master, mom, var, out, e, sc);
+    }
 }
 
 template <int NR, bool GB, bool PB, class R>
@@ -937,30 +944,33 @@ template <int NR, bool GB, bool PB, bool DS>
 __global__ void __launch_bounds__(kBlock)
 step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
                   float *__restrict__ mom, float *__restrict__ var, void *__restrict__ out,
-                  int dout, int64_t nvec, int head, int tail, int nt_state,
+                  int dout, int64_t nvec, int64_t nbw, int head, int tail, int nt_state,
                   ScalarArg<DS> sa) {
     const StepScalars sc = scalars(sa);
     const int n = NR > 0 ? NR : nrep;
-    if ((int64_t)blockIdx.x * kBlock >= nvec) {      // head and tail, as step_vec_kernel
+    constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
+    const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
+    const int64_t nfull = nvec / kBlock;
+    const int64_t w = blockIdx.x;
+    if (w < nbw) {                                   // full blocks, as step_vec_kernel
+        for (int64_t blk = w; blk < nfull; blk += nbw) {
+            if (nt_state)
+                step_block_split_shift<NR, GB, PB, true>(reps, n, pow2, master, mom, var, out,
+                                                         dout, blk, sc);
+            else
+                step_block_split_shift<NR, GB, PB, false>(reps, n, pow2, master, mom, var, out,
+                                                          dout, blk, sc);
+        }
+        return;
+    }
+    if (!(w == nbw && nfull * kBlock < nvec)) {      // head and tail, as step_vec_kernel
         for (int k = threadIdx.x; k < head + tail; k += kBlock) {
             const int64_t e = k < head ? (int64_t)(k - head) : nvec * kVec + (k - head);
             step_one<NR, GB, PB>(reps, n, master, mom, var, out, e, sc);
         }
         return;
     }
-    const int64_t blk = blockIdx.x;
-    constexpr bool kPow2 = NR > 0 && (NR & (NR - 1)) == 0;
-    const bool pow2 = kPow2 || (NR == 0 && sc.n_pow2);
-    if ((blk + 1) * kBlock <= nvec) {
-        if (nt_state)
-            step_block_split_shift<NR, GB, PB, true>(reps, n, pow2, master, mom, var, out, dout,
-                                                     blk, sc);
-        else
-            step_block_split_shift<NR, GB, PB, false>(reps, n, pow2, master, mom, var, out, dout,
-                                                      blk, sc);
-        return;
-    }
-    const int64_t j = blk * kBlock + threadIdx.x;
+    const int64_t j = nfull * kBlock + threadIdx.x;  // the partial block
     if (j >= nvec) return;
     const bool self_next = (threadIdx.x % 64) == 63 || j + 1 == nvec;
     float p[kVec], m[kVec], v[kVec];
@@ -1126,17 +1136,32 @@ hipError_t launch_fsdp_dtype(const FsdpArgs &a, hipStream_t stream) {
     }
 }
 
+// Workgroups that take the full blocks of a vector-path launch: one per
+// block, or at most a.max_workgroups (each then walks blocks at that stride).
+inline int64_t block_workgroups(const StepArgs &a, int64_t nfull) {
+    return (a.max_workgroups > 0 && a.max_workgroups < nfull) ? a.max_workgroups : nfull;
+}
+
+// Dynamic LDS a step launch reserves (and never touches) to cap the
+// workgroups per compute unit. A capped launch already holds few
+// workgroups per compute unit and reserves none, so that kernels on other
+// streams find LDS beside it.
+inline unsigned occupancy_lds(const StepArgs &a, unsigned lds) {
+    return a.max_workgroups > 0 ? 0u : lds;
+}
+
 template <int NR, bool GB, bool PB, bool DS>
 hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail,
                       hipStream_t stream) {
     Reps<NR> reps;
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
-    const int64_t grid = (nvec + kBlock - 1) / kBlock + (head + tail > 0 ? 1 : 0);
+    const int64_t nfull = nvec / kBlock, nbw = block_workgroups(a, nfull);
+    const int64_t grid = nbw + (nfull * kBlock < nvec ? 1 : 0) + (head + tail > 0 ? 1 : 0);
     // a dispatch holds at most 2^32-1 work-items
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
-                       ZK_STEP_LDS, stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, head, tail,
-                       a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
+                       occupancy_lds(a, ZK_STEP_LDS), stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, nbw, head,
+                       tail, a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
@@ -1244,11 +1269,13 @@ hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, int tail, hipStr
     }
     void *out = (char *)a.out + (int64_t)oe * h;
     const int dout = (int)(((uintptr_t)out % 16) / oe);
-    const int64_t grid = (nvec + kBlock - 1) / kBlock + (h + tail > 0 ? 1 : 0);
+    const int64_t nfull = nvec / kBlock, nbw = block_workgroups(a, nfull);
+    const int64_t grid = nbw + (nfull * kBlock < nvec ? 1 : 0) + (h + tail > 0 ? 1 : 0);
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((step_shift_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
-                       ZK_SHIFT_LDS, stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
-                       nvec, h, tail, a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
+                       occupancy_lds(a, ZK_SHIFT_LDS), stream, reps, a.n, a.master + h, a.m + h, a.v + h, out, dout,
+                       nvec, nbw, h, tail, a.stream_state ? 1 : 0,
+                       scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
