@@ -451,13 +451,35 @@ def check_adam_vs_torch_optim():
         assert diff < 2e-8, (t, diff)
 
 
-def check_adam_page_literal():
-    """The page's step lines evaluated by PyTorch on the CPU. m and v must
-    agree bit for bit (this fixes where the two fused multiply-adds sit).
-    torch's CPU square root is not always correctly rounded, so the page
-    code is run twice: once with the root taken in float64 and rounded to
-    float32 (correctly rounded, since 53 >= 2*24 + 2 bits), which must match
-    master bit for bit, and once with torch's own root, held to a few ulp."""
+def torch_adam(master, m, v, g, t, lr, b1, b2, eps, root=torch.sqrt):
+    """The Adam update of [ZF] "Implementing ZeRO's Adam from scratch"
+    (ZeroAdam.step) as equations over torch CPU tensors, returning new
+    (master, m, v):
+        m <- b1*m + (1-b1)*g            torch's scaled add
+        v <- b2*v + (1-b2)*g*g          torch's addcmul
+        master <- master - lr * (m/(1-b1^t)) / (root(v/(1-b2^t)) + eps)
+    with the bias corrections formed from Python floats, as the page does.
+    `root` is the square root used (torch's own by default)."""
+    m = torch.add(m * b1, g, alpha=1 - b1)
+    v = torch.addcmul(v * b2, g, g, value=1 - b2)
+    m_hat = m / (1 - b1 ** t)
+    v_hat = v / (1 - b2 ** t)
+    return master - lr * m_hat / (root(v_hat) + eps), m, v
+
+
+def _sqrt_rn(x: torch.Tensor) -> torch.Tensor:
+    """Correctly rounded binary32 square root: the root in binary64 (53 >=
+    2*24 + 2 bits, so one rounding to binary32 is correct)."""
+    return torch.from_numpy(np.sqrt(x.numpy().astype(np.float64)).astype(np.float32))
+
+
+def check_adam_equations_in_torch():
+    """The update equations evaluated by PyTorch on the CPU, against the
+    oracle over 10 steps of 8 bf16 replicas. m and v must agree bit for bit
+    (this fixes where the two fused multiply-adds sit). torch's CPU square
+    root is not always correctly rounded, so master is compared twice:
+    with a correctly rounded root (bit for bit) and with torch's own root
+    (within a few ulp)."""
     rng = np.random.default_rng(16)
     n, world = 200003, 8
     lr, (b1, b2), eps = 1e-3, (0.9, 0.999), 1e-8
@@ -465,44 +487,39 @@ def check_adam_page_literal():
     o = oracle.ShardOracle(n, 1, 0, lr, (b1, b2), eps, n_replicas=world)
     o.load_master(master0)
     out = np.zeros(n, np.float32)
-    master_cr = torch.from_numpy(master0.copy())
-    master_tq = torch.from_numpy(master0.copy())
-    m = torch.zeros(n)
-    v = torch.zeros(n)
+    zero_t = torch.zeros(n)
+    cr = (torch.from_numpy(master0.copy()), zero_t, zero_t)      # (master, m, v)
+    tq = cr
     for t in range(1, 11):
         reps = [_bf16_bits(torch.randn(n, generator=torch.Generator().manual_seed(100 * t + q)) * 1e-3)
                 for q in range(world)]
         g_np = oracle.reduce_mean(reps, 0, n, world)
         o.step(reps, t, out)
-        # reduce-scatter's sum in fp32, then the page's division
-        s = torch.from_numpy(_f32_from_bits(reps[0]).copy())
+        # the reduce-scatter's sum in fp32 in rank order, then the division
+        g = torch.stack([torch.from_numpy(_f32_from_bits(r)) for r in reps])
+        s_ = g[0].clone()
         for q in range(1, world):
-            s = s + torch.from_numpy(_f32_from_bits(reps[q]).copy())
-        g = s.clone()
-        g /= world
+            s_ = s_ + g[q]
+        g = s_ / world
         assert np.array_equal(g.numpy().view(np.uint32), g_np.view(np.uint32))
-        m.mul_(b1).add_(g, alpha=1 - b1)
-        v.mul_(b2).addcmul_(g, g, value=1 - b2)
-        m_hat = m / (1 - b1 ** t)
-        v_hat = v / (1 - b2 ** t)
-        root_cr = torch.from_numpy(np.sqrt(v_hat.numpy().astype(np.float64)).astype(np.float32))
-        master_cr -= lr * m_hat / (root_cr + eps)
-        master_tq -= lr * m_hat / (v_hat.sqrt() + eps)
-        assert np.array_equal(m.numpy().view(np.uint32), o.m.view(np.uint32)), t
-        assert np.array_equal(v.numpy().view(np.uint32), o.v.view(np.uint32)), t
-        assert np.array_equal(master_cr.numpy().view(np.uint32), o.master.view(np.uint32)), t
+        cr = torch_adam(*cr, g, t, lr, b1, b2, eps, root=_sqrt_rn)
+        tq = torch_adam(*tq, g, t, lr, b1, b2, eps)
+        assert np.array_equal(cr[1].numpy().view(np.uint32), o.m.view(np.uint32)), t
+        assert np.array_equal(cr[2].numpy().view(np.uint32), o.v.view(np.uint32)), t
+        assert np.array_equal(cr[0].numpy().view(np.uint32), o.master.view(np.uint32)), t
         # a 1-ulp root error moves u by ~lr * 2^-23; master may then round
         # the other way (one ulp of master)
-        diff = np.abs(master_tq.numpy().astype(np.float64) - o.master)
+        diff = np.abs(tq[0].numpy().astype(np.float64) - o.master)
         tol = t * (lr * 2.0**-21 + np.spacing(np.abs(o.master)).astype(np.float64))
         assert np.all(diff <= tol), (t, diff.max())
         assert np.array_equal(out.view(np.uint32), o.master.view(np.uint32))
 
 
-def check_toy_model_page_test():
-    """The page's own experiment, with 4 simulated ranks in one process:
-    sharded ZeroAdam (the oracle, one ShardOracle per rank, fp32 write-back)
-    against torch.optim.Adam on the full batch, 3 steps."""
+def check_toy_model_four_ranks():
+    """The toy experiment of [ZF] "Implementing ZeRO's Adam from scratch"
+    (a 64-256-10 MLP, a batch of 32 split over 4 ranks, 3 steps), with the 4
+    ranks simulated in one process: one ShardOracle per rank writing its fp32
+    slice, against torch.optim.Adam on the full batch."""
     gold = _golden("toy_model.json")
     world, lr, steps = gold["world"], gold["lr"], gold["steps"]
 

@@ -1,7 +1,7 @@
-"""The per-parameter dim-0 layout against FSDP2 itself, on the CPU with the
-gloo backend (the pages run their FSDP2 script the same way): the local
-shard shapes FSDP2 assigns, and the page's 3-step comparison with the
-oracle's per-parameter shards in place of FSDP2's optimizer."""
+"""The per-parameter dim-0 layout ([ZF] "ZeRO-3 and FSDP") against FSDP2
+itself, on the CPU with the gloo backend: the local shard shapes FSDP2
+assigns, and 3 Adam steps of FSDP2's own optimizer on those pieces against
+the oracle's shard step on the same reduced gradients (the page's 1e-5)."""
 import os
 import socket
 
@@ -24,38 +24,36 @@ def _make_model():
                                torch.nn.Linear(256, 10), torch.nn.Linear(10, 5))
 
 
+def _local(t):
+    """This rank's dim-0 piece of an FSDP2 parameter or gradient (a DTensor)."""
+    return t.to_local().detach().clone().numpy()
+
+
 def _worker(rank, world, port, outdir):
+    """Shard the model with FSDP2 (one group at the root: the per-parameter
+    dim-0 layout does not depend on the grouping), run 3 steps of its own
+    Adam on this rank's quarter of the batch, and save the local pieces:
+    shapes, initial values, the reduced gradients and the final values."""
     os.environ.update(MASTER_ADDR="127.0.0.1", MASTER_PORT=str(port))
-    import sys
-    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     from torch.distributed.device_mesh import init_device_mesh
     from torch.distributed.fsdp import fully_shard
     dist.init_process_group("gloo", rank=rank, world_size=world)
-    mesh = init_device_mesh("cpu", (world,))
+    model = fully_shard(_make_model(), mesh=init_device_mesh("cpu", (world,)))
+    head = torch.nn.Linear(5, 10)
     torch.manual_seed(123)
     X, Y = torch.randn(32, 64), torch.randint(0, 10, (32,))
-    model = _make_model()
-    for layer in model:
-        if isinstance(layer, torch.nn.Linear):
-            fully_shard(layer, mesh=mesh)
-    fully_shard(model, mesh=mesh)
-    head = torch.nn.Linear(5, 10)
-    loss_fn = torch.nn.CrossEntropyLoss()
-    opt = torch.optim.Adam(model.parameters(), lr=1e-2, foreach=False)
-    local0 = [p.to_local().detach().clone().numpy() for p in model.parameters()]
-    sl = slice(rank * 32 // world, (rank + 1) * 32 // world)
-    grads = []
-    for _ in range(3):
+    rows = slice(rank * 32 // world, (rank + 1) * 32 // world)
+    params = list(model.parameters())
+    opt = torch.optim.Adam(params, lr=1e-2, foreach=False)
+    saved = {f"s{k}": np.array(p.to_local().shape) for k, p in enumerate(params)}
+    saved.update({f"p0_{k}": _local(p) for k, p in enumerate(params)})
+    for t in range(3):
         opt.zero_grad()
-        loss_fn(head(model(X[sl])), Y[sl]).backward()
-        grads.append([p.grad.to_local().detach().clone().numpy() for p in model.parameters()])
+        torch.nn.functional.cross_entropy(head(model(X[rows])), Y[rows]).backward()
+        saved.update({f"g{t}_{k}": _local(p.grad) for k, p in enumerate(params)})
         opt.step()
-    local3 = [p.to_local().detach().clone().numpy() for p in model.parameters()]
-    np.savez(os.path.join(outdir, f"rank{rank}.npz"),
-             **{f"s{k}": np.array(a.shape) for k, a in enumerate(local0)},
-             **{f"p0_{k}": a for k, a in enumerate(local0)},
-             **{f"p3_{k}": a for k, a in enumerate(local3)},
-             **{f"g{t}_{k}": a for t, gl in enumerate(grads) for k, a in enumerate(gl)})
+    saved.update({f"p3_{k}": _local(p) for k, p in enumerate(params)})
+    np.savez(os.path.join(outdir, f"rank{rank}.npz"), **saved)
     dist.destroy_process_group()
 
 

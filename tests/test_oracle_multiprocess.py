@@ -1,13 +1,14 @@
-"""The page's 4-process experiment with real collectives (gloo, CPU), the
-oracle doing each rank's shard step.
+"""The toy experiment of [ZF] "Implementing ZeRO's Adam from scratch" with
+real collectives: 4 processes over gloo on the CPU, each with a quarter of
+the batch of a 64-256-10 MLP.
 
-Each of 4 processes builds the page's MLP, computes the gradient of its
-quarter of the batch, and then:
-  * ZeroAdam as the page writes it in torch: reduce_scatter_tensor (SUM),
-    divide by world, Adam on the slice, all_gather_into_tensor;
-  * the oracle: all_gather of every rank's flat gradient (the N replicas),
-    ShardOracle.step for this rank's slice, all_gather of the updated
-    slices.
+Each process steps two copies of the model:
+  * torch: the sharded step written from the method's definition with torch
+    collectives (reduce-scatter of the padded flat gradient, divide by the
+    world size, the Adam equations on this rank's slice, all-gather of the
+    updated slices);
+  * oracle: all-gather of every rank's flat gradient (the N replicas),
+    ShardOracle.step for this rank's slice, all-gather of the updated slices.
 After 3 steps both must match single-process torch.optim.Adam on the full
 batch within the page's 1e-5, and the oracle's shards must reassemble into
 a vector that equals the oracle run unsharded on the gathered replicas,
@@ -21,6 +22,7 @@ import numpy as np
 import torch
 import torch.distributed as dist
 import torch.multiprocessing as mp
+from torch.nn.utils import parameters_to_vector, vector_to_parameters
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -37,58 +39,50 @@ def _make_model():
                                torch.nn.Linear(256, 10))
 
 
-class PageZeroAdam:
-    """The page's ZeroAdam, restated in torch for the comparison."""
+def _padded(vec, length):
+    """vec followed by zeros up to `length` (the zero-padded flat vector)."""
+    return torch.nn.functional.pad(vec, (0, length - vec.numel()))
 
-    def __init__(self, params, lr, betas=(0.9, 0.999), eps=1e-8):
-        self.params = list(params)
-        self.lr, self.betas, self.eps, self.t = lr, betas, eps, 0
-        self.rank, self.world = dist.get_rank(), dist.get_world_size()
-        self.numel = sum(p.numel() for p in self.params)
-        self.shard = math.ceil(self.numel / self.world)
-        flat = self._flatten([p.data for p in self.params])
-        lo = self.rank * self.shard
-        self.master = flat[lo:lo + self.shard].clone()
-        self.m = torch.zeros_like(self.master)
-        self.v = torch.zeros_like(self.master)
 
-    def _flatten(self, tensors):
-        flat = torch.zeros(self.shard * self.world)
-        flat[:self.numel] = torch.cat([t.flatten() for t in tensors])
-        return flat
+def _torch_sharded_step(model, state, t, world, rank, lr, betas, eps):
+    """One data-parallel rank's ZeRO-2 step from the definitions, in torch.
+    state: this rank's fp32 slice (master, m, v) and the padded length."""
+    from oracle_pins import torch_adam
+    master, m, v, padded = state["master"], state["m"], state["v"], state["padded"]
+    shard = padded // world
+    grads = _padded(parameters_to_vector(p.grad for p in model.parameters()), padded)
+    g = torch.empty(shard)
+    dist.reduce_scatter_tensor(g, grads)                   # sum over the ranks
+    g = g / world
+    master, m, v = torch_adam(master, m, v, g, t, lr, betas[0], betas[1], eps)
+    state.update(master=master, m=m, v=v)
+    full = torch.empty(padded)
+    dist.all_gather_into_tensor(full, master)
+    vector_to_parameters(full[:sum(p.numel() for p in model.parameters())],
+                         model.parameters())
 
-    def step(self):
-        grads = self._flatten([p.grad for p in self.params])
-        g = torch.empty(self.shard)
-        dist.reduce_scatter_tensor(g, grads)
-        g /= self.world
-        self.t += 1
-        b1, b2 = self.betas
-        self.m.mul_(b1).add_(g, alpha=1 - b1)
-        self.v.mul_(b2).addcmul_(g, g, value=1 - b2)
-        m_hat = self.m / (1 - b1 ** self.t)
-        v_hat = self.v / (1 - b2 ** self.t)
-        self.master -= self.lr * m_hat / (v_hat.sqrt() + self.eps)
-        full = torch.empty(self.shard * self.world)
-        dist.all_gather_into_tensor(full, self.master)
-        offset = 0
-        for p in self.params:
-            p.data.copy_(full[offset:offset + p.numel()].view_as(p))
-            offset += p.numel()
+
+def _torch_sharded_state(model, world, rank):
+    numel = sum(p.numel() for p in model.parameters())
+    shard = math.ceil(numel / world)
+    flat = _padded(parameters_to_vector(model.parameters()).detach(), shard * world)
+    master = flat[rank * shard:(rank + 1) * shard].clone()
+    return dict(master=master, m=torch.zeros(shard), v=torch.zeros(shard),
+                padded=shard * world)
 
 
 def _worker(rank, world, port, outdir):
     os.environ.update(MASTER_ADDR="127.0.0.1", MASTER_PORT=str(port))
-    sys.path.insert(0, ROOT)
+    sys.path[:0] = [ROOT, os.path.join(ROOT, "tests")]
     import oracle
     dist.init_process_group("gloo", rank=rank, world_size=world)
     torch.manual_seed(123)
     X, Y = torch.randn(32, 64), torch.randint(0, 10, (32,))
     sl = slice(rank * 32 // world, (rank + 1) * 32 // world)
     loss_fn = torch.nn.CrossEntropyLoss()
-    ref, page_model, orc_model = _make_model(), _make_model(), _make_model()
+    ref, torch_model, orc_model = _make_model(), _make_model(), _make_model()
     opt_ref = torch.optim.Adam(ref.parameters(), lr=1e-2)
-    opt_page = PageZeroAdam(page_model.parameters(), lr=1e-2)
+    torch_state = _torch_sharded_state(torch_model, world, rank)
     numel = sum(p.numel() for p in orc_model.parameters())
     geo = oracle.geometry(numel, world, rank)
     P = geo["padded"]
@@ -102,10 +96,11 @@ def _worker(rank, world, port, outdir):
         opt_ref.zero_grad()
         loss_fn(ref(X), Y).backward()
         opt_ref.step()
-        for p in page_model.parameters():
+        for p in torch_model.parameters():
             p.grad = None
-        loss_fn(page_model(X[sl]), Y[sl]).backward()
-        opt_page.step()
+        loss_fn(torch_model(X[sl]), Y[sl]).backward()
+        with torch.no_grad():
+            _torch_sharded_step(torch_model, torch_state, t, world, rank, 1e-2, (0.9, 0.999), 1e-8)
         for p in orc_model.parameters():
             p.grad = None
         loss_fn(orc_model(X[sl]), Y[sl]).backward()
@@ -127,23 +122,23 @@ def _worker(rank, world, port, outdir):
             for p in orc_model.parameters():
                 p.copy_(torch.from_numpy(full[off:off + p.numel()]).view_as(p))
                 off += p.numel()
-    d_page = max(float((a - b).detach().abs().max()) for a, b in
-                 zip(ref.parameters(), page_model.parameters()))
+    d_torch = max(float((a - b).detach().abs().max()) for a, b in
+                  zip(ref.parameters(), torch_model.parameters()))
     d_orc = max(float((a - b).detach().abs().max()) for a, b in
                 zip(ref.parameters(), orc_model.parameters()))
-    d_po = max(float((a - b).detach().abs().max()) for a, b in
-               zip(page_model.parameters(), orc_model.parameters()))
+    d_to = max(float((a - b).detach().abs().max()) for a, b in
+               zip(torch_model.parameters(), orc_model.parameters()))
     np.save(os.path.join(outdir, f"r{rank}.npy"),
-            np.array([d_page, d_orc, d_po, float(bitexact)]))
+            np.array([d_torch, d_orc, d_to, float(bitexact)]))
     dist.destroy_process_group()
 
 
-def test_page_four_process_experiment(tmp_path):
+def test_toy_experiment_four_processes(tmp_path):
     world = 4
     mp.spawn(_worker, args=(world, _free_port(), str(tmp_path)), nprocs=world, join=True)
     for r in range(world):
-        d_page, d_orc, d_po, bitexact = np.load(tmp_path / f"r{r}.npy")
-        assert d_page < 1e-5, d_page           # the page's own claim
+        d_torch, d_orc, d_to, bitexact = np.load(tmp_path / f"r{r}.npy")
+        assert d_torch < 1e-5, d_torch         # the page's bound, torch sharded step
         assert d_orc < 1e-5, d_orc             # the oracle, sharded over 4 processes
-        assert d_po < 1e-6, d_po               # oracle vs the page's torch ZeroAdam
+        assert d_to < 1e-6, d_to               # oracle vs the torch sharded step
         assert bitexact == 1.0                 # shards reassemble the unsharded update
