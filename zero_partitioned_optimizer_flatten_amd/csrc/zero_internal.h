@@ -50,6 +50,9 @@ struct StepArgs {
     // for work on other streams; each workgroup then walks the blocks at a
     // stride of the cap, with the same per-element arithmetic.
     int64_t max_workgroups;
+    // Non-temporal hints on the replica loads of the vector path (set by
+    // the launcher from the streams' alignment).
+    bool nt_grad;
 };
 // MI355X's last-level (Infinity) cache in front of HBM.
 constexpr int64_t kInfinityCacheBytes = (int64_t)256 << 20;

@@ -68,8 +68,10 @@ constexpr int kGroup = 8;            // replicas loaded together
 #define ZK_FSDP_LDS 16384
 #endif
 // Non-temporal (streaming) hints. The replicas are read once and the
-// parameter output written once. For master/m/v the launcher chooses (see
-// StepArgs::stream_state): in the split lane layout of a full wavefront
+// parameter output written once (replica loads take the hint where every
+// stream sits on whole 128-byte lines; see StepArgs::nt_grad). For
+// master/m/v the launcher chooses (see StepArgs::stream_state): in the
+// split lane layout of a full wavefront
 // block, where every store instruction writes whole lines, non-temporal
 // loads and stores on them together measured 6% faster than the default
 // policy on a 875M-element shard (either hint alone: no gain, or slower),
@@ -318,24 +320,19 @@ template <bool GB> struct SplitRaw;
 template <> struct SplitRaw<true> { uint2 a, b; };
 template <> struct SplitRaw<false> { float4 a, b; };
 
-template <bool GB>
-__device__ __forceinline__ SplitRaw<GB> load_split(const void *base, int64_t q0);
-
-template <>
-__device__ __forceinline__ SplitRaw<true> load_split<true>(const void *base, int64_t q0) {
-    const uint2 *p = reinterpret_cast<const uint2 *>(base);
-    SplitRaw<true> r;
-    r.a = ld_u2<ZK_NT_GRAD>(p + q0);
-    r.b = ld_u2<ZK_NT_GRAD>(p + q0 + kBlock);
-    return r;
-}
-
-template <>
-__device__ __forceinline__ SplitRaw<false> load_split<false>(const void *base, int64_t q0) {
-    const float4 *p = reinterpret_cast<const float4 *>(base);
-    SplitRaw<false> r;
-    r.a = ld_f4<ZK_NT_GRAD>(p + q0);
-    r.b = ld_f4<ZK_NT_GRAD>(p + q0 + kBlock);
+// NTG: non-temporal hints on the replica loads (see StepArgs::nt_grad).
+template <bool GB, bool NTG>
+__device__ __forceinline__ SplitRaw<GB> load_split(const void *base, int64_t q0) {
+    SplitRaw<GB> r;
+    if constexpr (GB) {
+        const uint2 *p = reinterpret_cast<const uint2 *>(base);
+        r.a = ld_u2<NTG>(p + q0);
+        r.b = ld_u2<NTG>(p + q0 + kBlock);
+    } else {
+        const float4 *p = reinterpret_cast<const float4 *>(base);
+        r.a = ld_f4<NTG>(p + q0);
+        r.b = ld_f4<NTG>(p + q0 + kBlock);
+    }
     return r;
 }
 
@@ -366,13 +363,13 @@ __device__ __forceinline__ void store8_split(float *base, int64_t q0, const floa
     st_f4<NT>(p + q0 + kBlock, make_float4(x[4], x[5], x[6], x[7]));
 }
 
-template <int NR, bool GB>
+template <int NR, bool GB, bool NTG>
 __device__ __forceinline__ void fold_group_split(const Reps<NR> &reps, int q0r, int n,
                                                  int64_t q0, float (&s)[kVec]) {
     SplitRaw<GB> raw[kGroup];
 #pragma unroll
     for (int k = 0; k < kGroup; ++k)
-        if (q0r + k < n) raw[k] = load_split<GB>(reps.p[q0r + k], q0);
+        if (q0r + k < n) raw[k] = load_split<GB, NTG>(reps.p[q0r + k], q0);
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
         if (q0r + k < n) {
@@ -390,8 +387,9 @@ __device__ __forceinline__ void fold_group_split(const Reps<NR> &reps, int q0r, 
 }
 
 // The fused step on quads q0 and q0 + kBlock (split lane layout); NTS:
-// non-temporal hints on the master/m/v loads and stores.
-template <int NR, bool GB, bool PB, bool NTS>
+// non-temporal hints on the master/m/v loads and stores, NTG on the
+// replica loads.
+template <int NR, bool GB, bool PB, bool NTS, bool NTG>
 __device__ __forceinline__ void step_vector_split(const Reps<NR> &reps, int n, bool pow2,
                                                   float *__restrict__ master,
                                                   float *__restrict__ mom,
@@ -403,10 +401,10 @@ __device__ __forceinline__ void step_vector_split(const Reps<NR> &reps, int n, b
     float s[kVec];
     if constexpr (NR > 0 && NR <= 2 * kGroup) {
 #pragma unroll
-        for (int r = 0; r < NR; r += kGroup) fold_group_split<NR, GB>(reps, r, n, q0, s);
+        for (int r = 0; r < NR; r += kGroup) fold_group_split<NR, GB, NTG>(reps, r, n, q0, s);
     } else {
 #pragma unroll 1
-        for (int r = 0; r < n; r += kGroup) fold_group_split<NR, GB>(reps, r, n, q0, s);
+        for (int r = 0; r < n; r += kGroup) fold_group_split<NR, GB, NTG>(reps, r, n, q0, s);
     }
     float p[kVec], m[kVec], v[kVec];
     load8_split<NTS>(master, q0, p);
@@ -470,7 +468,7 @@ __device__ __forceinline__ const void *rep_base(const Reps<NR> &r, int q, int) {
 // one more, launched when head + tail > 0, steps the `head` elements just
 // before element 0 and the `tail` elements after the last vector one by
 // one, so a shard takes one launch whatever its alignment.
-template <int NR, bool GB, bool PB, bool DS>
+template <int NR, bool GB, bool PB, bool DS, bool NTG>
 __global__ void __launch_bounds__(kBlock)
 step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
                 float *__restrict__ mom, float *__restrict__ var,
@@ -486,10 +484,11 @@ step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
         for (int64_t blk = w; blk < nfull; blk += nbw) {
             const int64_t q0 = blk * 2 * kBlock + threadIdx.x;
             if (nt_state)
-                step_vector_split<NR, GB, PB, true>(reps, n, pow2, master, mom, var, out, q0, sc);
+                step_vector_split<NR, GB, PB, true, NTG>(reps, n, pow2, master, mom, var, out, q0,
+                                                         sc);
             else
-                step_vector_split<NR, GB, PB, false>(reps, n, pow2, master, mom, var, out, q0,
-                                                     sc);
+                step_vector_split<NR, GB, PB, false, NTG>(reps, n, pow2, master, mom, var, out,
+                                                          q0, sc);
         }
         return;
     }
@@ -594,9 +593,9 @@ __device__ __forceinline__ ShiftRaw<true> load_shift(const void *base, int d, in
                                                      bool self_next, ShiftRaw<true> *) {
     const uint4 *p = reinterpret_cast<const uint4 *>(base) + j;
     ShiftRaw<true> r;
-    r.a = ld_u4<ZK_NT_GRAD>(p);
+    r.a = ld_u4<false>(p);
     r.b = make_uint4(0u, 0u, 0u, 0u);
-    if (d && self_next) r.b = ld_u4<ZK_NT_GRAD>(p + 1);
+    if (d && self_next) r.b = ld_u4<false>(p + 1);
     return r;
 }
 
@@ -604,10 +603,10 @@ __device__ __forceinline__ ShiftRaw<false> load_shift(const void *base, int d, i
                                                       bool self_next, ShiftRaw<false> *) {
     const float4 *p = reinterpret_cast<const float4 *>(base) + 2 * j;
     ShiftRaw<false> r;
-    r.a = ld_f4<ZK_NT_GRAD>(p);
-    r.b = ld_f4<ZK_NT_GRAD>(p + 1);
+    r.a = ld_f4<false>(p);
+    r.b = ld_f4<false>(p + 1);
     r.c = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (d && self_next) r.c = ld_f4<ZK_NT_GRAD>(p + 2);
+    if (d && self_next) r.c = ld_f4<false>(p + 2);
     return r;
 }
 
@@ -758,9 +757,11 @@ __device__ __forceinline__ void store_f32x8_at(float *q, int d, const float (&x)
 // fp32. A replica d elements past its 16-byte base starts its quads r =
 // d mod 4 elements into a unit, so a lane's quad spans its own unit and
 // the next. The next unit of half 0 and of half 1 is the next lane's (DPP
-// wave shift); lane 63 loads both of its next units itself: the block's
-// second half starts there, and past it the unit holds the block's last
-// element, so no read leaves the units of the buffer's own elements.
+// wave shift). For lane 63, half 0's next unit is lane 0's unit of half 1
+// (read across lanes; loading it again measured 0.8 points slower), and
+// half 1's next unit, past the block, it loads itself: that unit holds the
+// block's last element, so no read leaves the units of the buffer's own
+// elements.
 template <bool GB> struct UnitT;
 template <> struct UnitT<true> { typedef uint2 T; };
 template <> struct UnitT<false> { typedef uint4 T; };
@@ -769,12 +770,30 @@ __device__ __forceinline__ uint2 next_lane(uint2 v) {
     return make_uint2(next_lane(v.x), next_lane(v.y));
 }
 
+// Lane 0's value of v, in every lane.
+__device__ __forceinline__ uint2 first_lane(uint2 v) {
+    return make_uint2((uint32_t)__builtin_amdgcn_readlane((int)v.x, 0),
+                      (uint32_t)__builtin_amdgcn_readlane((int)v.y, 0));
+}
+
+__device__ __forceinline__ uint4 first_lane(uint4 v) {
+    return make_uint4((uint32_t)__builtin_amdgcn_readlane((int)v.x, 0),
+                      (uint32_t)__builtin_amdgcn_readlane((int)v.y, 0),
+                      (uint32_t)__builtin_amdgcn_readlane((int)v.z, 0),
+                      (uint32_t)__builtin_amdgcn_readlane((int)v.w, 0));
+}
+
+// Off-phase replicas straddle 128-byte lines: the line a block shares with
+// the next block (on another XCD) is fetched twice. With the default cache
+// policy the second fetch finds it in the Infinity Cache; non-temporal
+// loads measured slower here (75.1% against 75.7% of peak HBM bandwidth,
+// seven replicas one element off, 7e9-element shard).
 template <bool GB>
 __device__ __forceinline__ typename UnitT<GB>::T load_unit(const void *base, int64_t u) {
     if constexpr (GB) {
-        return ld_u2<ZK_NT_GRAD>(reinterpret_cast<const uint2 *>(base) + u);
+        return ld_u2<false>(reinterpret_cast<const uint2 *>(base) + u);
     } else {
-        return ld_u4<ZK_NT_GRAD>(reinterpret_cast<const uint4 *>(base) + u);
+        return ld_u4<false>(reinterpret_cast<const uint4 *>(base) + u);
     }
 }
 
@@ -823,10 +842,8 @@ __device__ __forceinline__ void fold_group_split_shift(const ShiftReps<NR> &reps
             const int64_t u = ub + (GB ? d / 4 : 0);
             raw[k].a[0] = load_unit<GB>(reps.p[q0 + k], u);
             raw[k].a[1] = load_unit<GB>(reps.p[q0 + k], u + kBlock);
-            if ((d & 3) && lane == 63) {
-                raw[k].nx[0] = load_unit<GB>(reps.p[q0 + k], u + 1);
+            if ((d & 3) && lane == 63)         // past the block: lane 63 loads it
                 raw[k].nx[1] = load_unit<GB>(reps.p[q0 + k], u + kBlock + 1);
-            }
         }
     }
 #pragma unroll
@@ -836,9 +853,13 @@ __device__ __forceinline__ void fold_group_split_shift(const ShiftReps<NR> &reps
             if (r) {
                 const typename UnitT<GB>::T n0 = next_lane(raw[k].a[0]);
                 const typename UnitT<GB>::T n1 = next_lane(raw[k].a[1]);
+                // the unit after half 0 is lane 0's unit of half 1
+                const typename UnitT<GB>::T h1 = first_lane(raw[k].a[1]);
                 if (lane != 63) {
                     raw[k].nx[0] = n0;
                     raw[k].nx[1] = n1;
+                } else {
+                    raw[k].nx[0] = h1;
                 }
             } else {
                 raw[k].nx[0] = raw[k].a[0];
@@ -1068,9 +1089,11 @@ fsdp_step_kernel(FsdpBatch<NR> b, int nrep, float *__restrict__ master,
     if (aligned && (chunk + 1) * kBlock * kVec <= numel) {
         const int64_t q0 = chunk * 2 * kBlock + threadIdx.x;
         if (nt_state)
-            step_vector_split<NR, GB, PB, true>(reps, n, pow2, ms, mm, vs, out, q0, sc);
+            step_vector_split<NR, GB, PB, true, ZK_NT_GRAD>(reps, n, pow2, ms, mm, vs, out, q0,
+                                                            sc);
         else
-            step_vector_split<NR, GB, PB, false>(reps, n, pow2, ms, mm, vs, out, q0, sc);
+            step_vector_split<NR, GB, PB, false, ZK_NT_GRAD>(reps, n, pow2, ms, mm, vs, out, q0,
+                                                             sc);
         return;
     }
     const int64_t j = chunk * kBlock + threadIdx.x;     // vector index
@@ -1159,9 +1182,19 @@ hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail,
     const int64_t grid = nbw + (nfull * kBlock < nvec ? 1 : 0) + (head + tail > 0 ? 1 : 0);
     // a dispatch holds at most 2^32-1 work-items
     if (grid > (int64_t)(0xFFFFFFFFu / kBlock)) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS>), dim3((unsigned)grid), dim3(kBlock),
-                       occupancy_lds(a, ZK_STEP_LDS), stream, reps, a.n, a.master, a.m, a.v, a.out, nvec, nbw, head,
-                       tail, a.stream_state ? 1 : 0, scalar_arg<DS>(a.sc, a.sc_dev));
+    // replica cache policy as a template parameter: a runtime choice inside
+    // the kernel measured 2 points slower on line-aligned streams
+    const dim3 g((unsigned)grid), b(kBlock);
+    const unsigned lds = occupancy_lds(a, ZK_STEP_LDS);
+    const int nts = a.stream_state ? 1 : 0;
+    if (a.nt_grad)
+        hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS, true>), g, b, lds, stream, reps, a.n,
+                           a.master, a.m, a.v, a.out, nvec, nbw, head, tail, nts,
+                           scalar_arg<DS>(a.sc, a.sc_dev));
+    else
+        hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS, false>), g, b, lds, stream, reps,
+                           a.n, a.master, a.m, a.v, a.out, nvec, nbw, head, tail, nts,
+                           scalar_arg<DS>(a.sc, a.sc_dev));
     return hipGetLastError();
 }
 
@@ -1318,6 +1351,12 @@ hipError_t step_typed(const StepArgs &a, hipStream_t stream) {
     const int64_t nvec = (a.shard - h) / kVec;
     const int tail = (int)(a.shard - h - nvec * kVec);
     StepArgs b = a;
+    // non-temporal replica loads only where every stream sits on whole
+    // 128-byte lines: with the 16-byte head, blocks straddle lines and the
+    // default policy lets a shared line's second fetch hit the Infinity
+    // Cache (measured 76.7% against 73.9% of peak HBM bandwidth, eight
+    // replicas 16 bytes off a line, 7e9-element shard; level on lines)
+    b.nt_grad = ZK_NT_GRAD && all_at(a, h, kLine);
     const void *shifted[ZERO_MAX_WORLD];
     const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
     for (int q = 0; q < a.n; ++q) shifted[q] = (const char *)a.grads[q] + (int64_t)ge * h;
