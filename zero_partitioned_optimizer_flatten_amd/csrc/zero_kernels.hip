@@ -1443,15 +1443,19 @@ __global__ void __launch_bounds__(kCopyBlock) copy_segments_kernel(SegBatch b) {
 
 // ---------------------------------------------------------- master load
 // master[i] = fp32(flat[i]), m[i] = v[i] = 0. The launcher starts the vector
-// range at the first element h where master, m and v are 16-byte aligned.
+// range at the first element h where master, m and v sit on a 128-byte
+// line, so that every store instruction writes whole lines (blocks that
+// split lines with the next block's workgroup, on another XCD, measured
+// 60% of peak HBM bandwidth on the Llama-13B rank-7 shard).
 // A full wavefront block (8 * kBlock elements) takes the split lane layout
 // of the fused step: lane l writes the quads l and l + kBlock, so every
 // store instruction covers one contiguous 1 KiB span of each state array.
-// With SA (the source shares the state's phase: a bf16 quad on 8 bytes, an
-// fp32 quad on 16) a lane reads its quad with one load; otherwise with one
-// load per element (consecutive lanes still read consecutive quads). The
-// h head elements and the tail after the last full block take one extra
-// workgroup, element by element.
+// A lane reads its source quad (8 bytes of bf16, 16 of fp32) with one wide
+// load: non-temporal where the source shares the state's 16-byte phase
+// (SA), a plain one at the source's own alignment otherwise (gfx950 takes
+// wide global loads at any element alignment). The h head elements and the
+// tail after the last full block take one extra workgroup, element by
+// element.
 template <bool FB>
 __device__ __forceinline__ float src_elem(const void *flat, int64_t i) {
     return FB ? widen_bf16(reinterpret_cast<const uint16_t *>(flat)[i])
@@ -1460,15 +1464,19 @@ __device__ __forceinline__ float src_elem(const void *flat, int64_t i) {
 
 template <bool FB, bool SA>
 __device__ __forceinline__ float4 src_quad(const void *flat, int64_t e) {
-    if constexpr (SA && FB) {
-        const uint2 w = ld_u2<true>(reinterpret_cast<const uint16_t *>(flat) + e);
+    if constexpr (FB) {
+        const uint16_t *p = reinterpret_cast<const uint16_t *>(flat) + e;
+        uint2 w;
+        if constexpr (SA) w = ld_u2<true>(p);
+        else __builtin_memcpy(&w, p, sizeof w);
         return make_float4(widen_bf16(w.x & 0xFFFFu), widen_bf16(w.x >> 16),
                            widen_bf16(w.y & 0xFFFFu), widen_bf16(w.y >> 16));
-    } else if constexpr (SA) {
-        return ld_f4<true>(reinterpret_cast<const float *>(flat) + e);
     } else {
-        return make_float4(src_elem<FB>(flat, e), src_elem<FB>(flat, e + 1),
-                           src_elem<FB>(flat, e + 2), src_elem<FB>(flat, e + 3));
+        const float *p = reinterpret_cast<const float *>(flat) + e;
+        if constexpr (SA) return ld_f4<true>(p);
+        float4 v;
+        __builtin_memcpy(&v, p, sizeof v);
+        return v;
     }
 }
 
@@ -1630,12 +1638,11 @@ hipError_t launch_load_master(const void *flat, bool flat_bf16, float *master, f
                               float *v, int64_t shard, hipStream_t stream) {
     if (shard <= 0) return hipSuccess;
     constexpr int64_t per = (int64_t)kVec * kBlock;
-    // master, m and v share their phase within 16 bytes (the context
-    // allocates them that way); h puts them on a 16-byte boundary
-    int head = (int)(((16u - ((uintptr_t)master & 15u)) & 15u) / 4u);
-    if (((uintptr_t)m & 15u) != ((uintptr_t)master & 15u) ||
-        ((uintptr_t)v & 15u) != ((uintptr_t)master & 15u))
-        return hipErrorInvalidValue;
+    // master, m and v share their phase within a line (the context
+    // allocates them that way); h puts them on a 128-byte line
+    const uintptr_t ph = (uintptr_t)master & 127u;
+    int head = (int)(((128u - ph) & 127u) / 4u);
+    if (((uintptr_t)m & 127u) != ph || ((uintptr_t)v & 127u) != ph) return hipErrorInvalidValue;
     if (head > shard) head = (int)shard;
     const int64_t nblk = (shard - head) / per;
     const int64_t grid = nblk + ((shard - nblk * per) > 0 ? 1 : 0);
@@ -1656,8 +1663,8 @@ hipError_t launch_load_master(const void *flat, bool flat_bf16, float *master, f
             hipLaunchKernelGGL((load_master_kernel<false, true>), g, blk, 0, stream, flat, master,
                                m, v, shard, head, nblk);
         else
-            hipLaunchKernelGGL((load_master_kernel<false, false>), g, blk, 0, stream, flat, master,
-                               m, v, shard, head, nblk);
+            hipLaunchKernelGGL((load_master_kernel<false, false>), g, blk, 0, stream, flat,
+                               master, m, v, shard, head, nblk);
     }
     return hipGetLastError();
 }
