@@ -348,9 +348,14 @@ int zero_fsdp_step_sched(zero_ctx *ctx, const void *const *grads,
                          void *const *params_out, zero_dtype param_dtype,
                          hipStream_t stream);
 
-/* Copy the fp32 state out of / into the context (checkpoint and resume).
+/* Copy the fp32 state out of / into the context (checkpoint and resume):
+ * the master copy of this rank's slice and the two moments that [ZeRO and
+ * FSDP], ZeroAdam constructor, creates per rank (master = the slice of the
+ * flat parameters, m = v = 0). The step count is the caller's (the t of
+ * zero_step) or the schedule's (zero_schedule_get / zero_schedule_init).
  * master, m, v: device pointers to `shard` floats each; any may be NULL to
- * skip that buffer. Stream-ordered device-to-device copies. */
+ * skip that buffer. Stream-ordered device-to-device copies. EINVAL: null
+ * context, or a buffer shorter than `shard` floats within its allocation. */
 int zero_get_state(const zero_ctx *ctx, float *master, float *m, float *v,
                    hipStream_t stream);
 int zero_set_state(zero_ctx *ctx, const float *master, const float *m,

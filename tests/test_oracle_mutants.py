@@ -49,6 +49,7 @@ MUTANTS = [
     ("dim0_floor", "    if (c * world < d0)\n        c += 1;", "    if (c * world < d0)\n        c += 0;"),
     ("dim0_no_clamp", "    if (first > d0) first = d0;\n", ""),
     ("state_two_tensors", "return 3 * shard * (int64_t)sizeof(float);", "return 2 * shard * (int64_t)sizeof(float);"),
+    ("unflatten_misses_offset", "memcpy(dsts[t], in + off * elem_size,", "memcpy(dsts[t], in,"),
 ]
 
 
