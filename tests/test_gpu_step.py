@@ -284,6 +284,53 @@ def test_flatten_ragged_bitexact(dtype):
             st.close()
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_flatten_every_phase_pair(dtype):
+    """Every pair of (source, destination) offsets within 16 bytes, plus
+    destinations deeper into a 128-byte line: the destination flat buffer is
+    a view at element offset b, the sources are carved from one buffer
+    starting at element offset a. The list holds a
+    tensor of several copy chunks and a ragged tail, a 1-element tensor and
+    a tensor shorter than 16 bytes, so heads, wide bodies and tails all run.
+    flatten equals the oracle byte for byte and the guard elements before
+    and after the destination keep their fill; unflatten back into views at
+    offset a gives the sources back and leaves their neighbours alone."""
+    dev = torch.device("cuda")
+    ph = 16 // (2 if dtype == torch.bfloat16 else 4)
+    ity = torch.int16 if dtype == torch.bfloat16 else torch.int32
+    nty = np.int16 if dtype == torch.bfloat16 else np.int32
+    sizes = [5 * 1024 + 13, 1, 3, 777]
+    numel = sum(sizes)
+    st = zero.ShardState(numel, 3, 0, 1e-3)
+    P = st.padded
+    vals = synth.gaussian(numel + ph, 1.0, 11, dtype).to(dev)
+    for a in range(ph):
+        srcs, off = [], a
+        for k in sizes:
+            srcs.append(vals[off:off + k])
+            off += k
+        src_bits = [bits(x) for x in srcs]
+        want = oracle.flatten(src_bits, P, fill=0x5A)
+        for b in list(range(ph)) + [5 * ph + 2, 8 * ph - 1]:
+            buf = torch.full((P + 9 * ph,), -1, dtype=ity, device=dev).view(dtype)
+            st.flatten(srcs, buf[b:b + P])
+            got = bits(buf)
+            assert got[b:b + P].tobytes() == want.tobytes(), (a, b)
+            guard = np.concatenate([got[:b], got[b + P:]])
+            assert (guard.view(nty) == -1).all(), (a, b)
+            back = torch.full((numel + 2 * ph,), -1, dtype=ity, device=dev).view(dtype)
+            dsts, off = [], a
+            for k in sizes:
+                dsts.append(back[off:off + k])
+                off += k
+            st.unflatten(buf[b:b + P], dsts)
+            bb = bits(back)
+            assert bb[a:a + numel].tobytes() == np.concatenate(src_bits).tobytes(), (a, b)
+            assert (np.concatenate([bb[:a], bb[a + numel:]]).view(nty) == -1).all(), (a, b)
+    log(f"flatten/unflatten {dtype}: all {ph}x{ph} phase pairs equal the oracle")
+    st.close()
+
+
 def test_flatten_gpt2_list():
     shapes = synth.gpt2_small_shapes()
     numel = synth.numel_of(shapes)
