@@ -182,6 +182,79 @@ def test_graph_of_bucketed_step():
     st.close()
 
 
+def test_graph_of_the_whole_hot_path():
+    """One training step's optimizer path captured as one graph: flatten of
+    this rank's gradient list into its full flat buffer, the scheduled step
+    over the N full flat replicas (the pages' layout) writing bf16 into the
+    full flat parameter buffer at lo, and unflatten of that buffer into the
+    parameter tensors. The gradient list is ragged and carved from one
+    buffer at an odd element offset; rank 3 holds the pad. Each replay, with
+    new gradients and eager work between replays and an lr change before
+    one of them, equals the oracle's flatten, step and unflatten."""
+    shapes = synth.ragged_shapes(5, 23, 30_000) + [(1,), (7, 3)]
+    numel = synth.numel_of(shapes)
+    world, rank = 4, 3
+    dev = "cuda"
+    st = zero.ShardState(numel, world, rank, 1e-3, BETAS, EPS)
+    orc = oracle.ShardOracle(numel, world, rank, 1e-3, BETAS, EPS)
+    S, lo, P = st.shard, st.lo, st.padded
+    assert P > numel, "rank 3 should hold pad elements"
+    flat_p = torch.zeros(P, dtype=torch.float32, device=dev)
+    flat_p[:numel] = synth.gaussian(numel, synth.PARAM_STD, synth.PARAM_SEED, torch.float32, dev)
+    st.load_master(flat_p)
+    orc.load_master(bits(flat_p))
+    storage = torch.zeros(numel + 1, dtype=torch.bfloat16, device=dev)
+    own_list = synth.split_views(storage[1:], shapes)
+    own_flat = torch.full((P,), -1, dtype=torch.int16, device=dev).view(torch.bfloat16)
+    peers = {q: torch.zeros(P, dtype=torch.bfloat16, device=dev) for q in range(world) if q != rank}
+    reps = [own_flat if q == rank else peers[q] for q in range(world)]
+    param_flat = flat_p.to(torch.bfloat16)
+    params = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in shapes]
+    want_flat = bits(param_flat)
+
+    def fill(t):
+        synth.fill_gaussian(storage[1:], 1e-3, synth.grad_seed(t, rank))
+        for q, b in peers.items():
+            synth.fill_gaussian(b[:numel], 1e-3, synth.grad_seed(t, q))
+
+    def path():
+        st.flatten(own_list, own_flat)
+        st.step_sched(reps, param_flat)
+        st.unflatten(param_flat, params)
+
+    def check(label, t):
+        own_ref = oracle.flatten([bits(x) for x in own_list], P)
+        orc.step([own_ref if q == rank else bits(peers[q]) for q in range(world)], t, want_flat)
+        torch.cuda.synchronize()
+        assert bits(own_flat).tobytes() == own_ref.tobytes(), (label, t)
+        assert_bitexact_state(f"{label} t={t}", gpu_state(st), [orc.master, orc.m, orc.v],
+                              bits(param_flat), want_flat)
+        for a, b in zip(params, oracle.unflatten(want_flat, shapes)):
+            assert bits(a).tobytes() == b.tobytes(), (label, t)
+
+    st.schedule(1)
+    fill(1)
+    path()                                        # eager step 1 (also loads the code)
+    check("whole path eager", 1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    torch.cuda.synchronize()
+    assert st.schedule_next_t() == 2              # capture launched nothing
+    scratch = torch.empty(1 << 20, device=dev)
+    for t in range(2, 8):
+        fill(t)
+        scratch.normal_()                         # unrelated eager work
+        if t == 5:
+            st.schedule_lr(5e-4)                  # reaches the next replay
+            orc.lr = 5e-4
+        g.replay()
+        check("whole path graph", t)
+        log(f"whole-path graph replay t={t} bit-exact")
+    del g
+    st.close()
+
+
 def test_fsdp_scheduled_and_graph():
     """The per-parameter layout: scheduled steps, eager and replayed,
     against host-t steps on an identical second state."""
