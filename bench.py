@@ -66,8 +66,14 @@ def step_bytes_per_elem(world, grad_bytes=2, param_bytes=2):
 
 
 def kernel_source_digest():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """First 16 hex digits of the sha256 of the kernel source's code, with
+    comments removed and whitespace collapsed: an edit that changes no code
+    keeps the committed counters valid, any other edit invalidates them."""
+    with open(KERNEL_SRC) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return hashlib.sha256(" ".join(text.split()).encode()).hexdigest()[:16]
 
 
 def measured_traffic():

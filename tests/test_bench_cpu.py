@@ -45,3 +45,17 @@ def test_unknown_extras_are_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2 and "unknown extras: nope" in r.stderr
     assert set(bench.EXTRAS) == {"buckets", "graph", "gemm", "partition", "lists", "fsdp"}
+
+
+def test_kernel_code_digest(tmp_path, monkeypatch):
+    """The digest that gates the committed counters ignores comments and
+    whitespace and changes with any code edit."""
+    src = tmp_path / "k.hip"
+    code = "// header\n__global__ void k(int *p) {\n  p[0] = 1; /* store */\n}\n"
+    src.write_text(code)
+    monkeypatch.setattr(bench, "KERNEL_SRC", str(src))
+    d0 = bench.kernel_source_digest()
+    src.write_text("// other words\n\n__global__  void k(int *p)\n{ p[0] = 1;\n}\n")
+    assert bench.kernel_source_digest() == d0
+    src.write_text(code.replace("= 1", "= 2"))
+    assert bench.kernel_source_digest() != d0

@@ -40,8 +40,10 @@ constexpr int kVec = 8;              // elements per lane per vector step
 constexpr int kGroup = 8;            // replicas loaded together
 
 // Launch shape of the fused step: one 8-element vector per lane and one pass
-// over the shard (no grid-stride loop), so the waves in flight at any moment
-// cover one contiguous, sliding window of every stream.
+// over the shard, one block per workgroup (a workgroup cap, which leaves room
+// for kernels on other streams, makes each workgroup stride over blocks), so
+// the waves in flight at any moment cover one contiguous, sliding window of
+// every stream.
 //
 // Dynamic LDS reserved (unused) per fused-step workgroup: caps how many
 // workgroups share a CU (160 KiB of LDS per CU). The default keeps six
@@ -70,15 +72,15 @@ constexpr int kGroup = 8;            // replicas loaded together
 // Non-temporal (streaming) hints. The replicas are read once and the
 // parameter output written once (replica loads take the hint where every
 // stream sits on whole 128-byte lines; see StepArgs::nt_grad). For
-// master/m/v the launcher chooses (see StepArgs::stream_state): in the
-// split lane layout of a full wavefront
-// block, where every store instruction writes whole lines, non-temporal
-// loads and stores on them together measured 6% faster than the default
-// policy on a 875M-element shard (either hint alone: no gain, or slower),
-// but slower on shards whose state fits in the 256 MB Infinity Cache and
-// stays there between steps. Where a lane owns 32 contiguous bytes (the
-// last partial block, the element and shifted paths), the hints measured
-// slower, so those accesses keep the default policy.
+// master/m/v the launcher chooses (see StepArgs::stream_state): in the split
+// lane layout of a full wavefront block, where every store instruction
+// writes whole lines, non-temporal loads and stores on them together
+// measured 6% faster than the default policy on a 875M-element shard
+// (either hint alone: no gain, or slower), but slower on shards whose state
+// fits in the 256 MB Infinity Cache and stays there between steps. Where a
+// lane owns 32 contiguous bytes (the last partial block, the element and
+// shifted paths), the hints measured slower, so those accesses keep the
+// default policy.
 #ifndef ZK_NT_GRAD
 #define ZK_NT_GRAD 1
 #endif
@@ -459,9 +461,9 @@ __device__ __forceinline__ const void *rep_base(const Reps<NR> &r, int q, int) {
 
 // Vector path: every stream 16-byte aligned. A full wavefront block takes
 // the split lane layout; the last, partial block has lane j - 64*block
-// handle elements [8j, 8j+8) of vector j. NR > 0 fixes the replica count at compile time
-// (N <= 16 fully unrolled; larger N walks the groups in a loop to bound
-// register use); NR == 0 reads it from `nrep`. Workgroups [0, nbw) take
+// handle elements [8j, 8j+8) of vector j. NR > 0 fixes the replica count at
+// compile time (N <= 16 fully unrolled; larger N walks the groups in a loop
+// to bound register use); NR == 0 reads it from `nrep`. Workgroups [0, nbw) take
 // the full blocks: block w, then w + nbw, ... (nbw = the number of full
 // blocks unless the launch is capped, so normally one block each, one pass
 // over the shard). The next workgroup takes the partial block, if any, and
