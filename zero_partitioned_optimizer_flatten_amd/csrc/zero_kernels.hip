@@ -90,6 +90,14 @@ constexpr int kGroup = 8;            // replicas loaded together
 #ifndef ZK_NT_COPY
 #define ZK_NT_COPY 1
 #endif
+// Master initialisation: dynamic LDS reserved (unused) per one-wave
+// workgroup, six per compute unit as for the fused step. Its three write
+// streams (master, m, v) and one read stream measured 80.7% / 80.1% of peak
+// HBM bandwidth at six per CU against 70.2% / 65.5% uncapped (7e9/N=8 and
+// 70e9/N=64 shards; four, five, eight and ten per CU 65.7-80.6%).
+#ifndef ZK_K0_LDS
+#define ZK_K0_LDS 26624
+#endif
 // Segment copy: workgroup size (one 16-byte vector per lane per chunk).
 #ifndef ZK_COPY_BLOCK
 #define ZK_COPY_BLOCK 64
@@ -1697,17 +1705,17 @@ hipError_t launch_load_master(const void *flat, bool flat_bf16, float *master, f
     const dim3 g((unsigned)grid), blk(kBlock);
     if (flat_bf16) {
         if (sa)
-            hipLaunchKernelGGL((load_master_kernel<true, true>), g, blk, 0, stream, flat, master,
+            hipLaunchKernelGGL((load_master_kernel<true, true>), g, blk, ZK_K0_LDS, stream, flat, master,
                                m, v, shard, head, nblk);
         else
-            hipLaunchKernelGGL((load_master_kernel<true, false>), g, blk, 0, stream, flat, master,
+            hipLaunchKernelGGL((load_master_kernel<true, false>), g, blk, ZK_K0_LDS, stream, flat, master,
                                m, v, shard, head, nblk);
     } else {
         if (sa)
-            hipLaunchKernelGGL((load_master_kernel<false, true>), g, blk, 0, stream, flat, master,
+            hipLaunchKernelGGL((load_master_kernel<false, true>), g, blk, ZK_K0_LDS, stream, flat, master,
                                m, v, shard, head, nblk);
         else
-            hipLaunchKernelGGL((load_master_kernel<false, false>), g, blk, 0, stream, flat,
+            hipLaunchKernelGGL((load_master_kernel<false, false>), g, blk, ZK_K0_LDS, stream, flat,
                                master, m, v, shard, head, nblk);
     }
     return hipGetLastError();
