@@ -56,11 +56,12 @@ constexpr int kGroup = 8;            // replicas loaded together
 #endif
 // The same for the shifted path, which does more per lane (cross-lane
 // realignment, the last lane's own loads, narrow stores) and measured best
-// with more waves: ten per CU gave 75.5-77.5% of peak HBM bandwidth against
-// 71.9-74.9% at seven, 74.4-75.9% at twelve and 69.4-73.8% at sixteen
-// (7e9-element shard, N = 8, one or seven replicas off the state's phase).
+// with more waves: twelve per CU gave 77.8% / 77.6% of peak HBM bandwidth
+// against 76.9% / 74.6% at ten, 74.6% / 75.9% at fourteen and 72.9% / 73.9%
+// at sixteen (7e9-element shard, N = 8; seven replicas one element off the
+// state's phase / one replica and the output three off).
 #ifndef ZK_SHIFT_LDS
-#define ZK_SHIFT_LDS 16384
+#define ZK_SHIFT_LDS 13312
 #endif
 // The same for the per-parameter step, whose workgroups first search the
 // segment table (dependent scalar loads) before their first vector load:
