@@ -102,6 +102,12 @@ int zero_shard_init(int64_t numel, int32_t world, int32_t rank,
 int zero_shard_info(const zero_ctx *ctx, int64_t *shard, int64_t *lo,
                     int64_t *padded);
 
+/* Bytes of optimizer state this rank holds ([ZeRO and FSDP], ZeroAdam's
+ * state_bytes: fp32 master, m and v of its elements, 12 bytes each): 12 *
+ * shard for the flat layout, 12 * (its rows of every parameter) for the
+ * per-parameter layout. Host only. EINVAL: null context or bytes. */
+int zero_shard_state_bytes(const zero_ctx *ctx, int64_t *bytes);
+
 /* Change the learning rate used by later steps (schedules). EINVAL if not
  * finite. Host only. */
 int zero_set_lr(zero_ctx *ctx, double lr);

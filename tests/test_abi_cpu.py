@@ -69,6 +69,9 @@ def test_state_bytes_rejects():
         zero.state_bytes(4, 1e9, 8)
     with pytest.raises(zero.ZeroError):
         zero.state_bytes(2, 1e9, 0)
+    out = ctypes.c_int64(-1)
+    assert zero.lib().zero_shard_state_bytes(None, ctypes.byref(out)) == zero.ZERO_EINVAL
+    assert out.value == -1
 
 
 def _init(*a):

@@ -44,6 +44,8 @@ def test_page_experiment_through_the_library():
     states = [zero.ShardState(numel, WORLD, r, LR) for r in range(WORLD)]
     S, P = states[0].shard, states[0].padded
     assert (numel, S) == (19_210, 4_803)                 # the page's toy model
+    # the page's state_bytes per rank (12 bytes per shard element: 57,636)
+    assert [st.state_bytes() for st in states] == [oracle.state_bytes(S)] * WORLD == [57_636] * WORLD
 
     flat_params = torch.empty(P, dtype=torch.float32, device=dev)
     states[0].flatten([p.detach() for p in params], flat_params)
@@ -103,6 +105,11 @@ def test_page_fsdp_experiment_through_the_library():
     shapes = [tuple(p.shape) for p in params]
     states = [zero.FsdpShardState(shapes, WORLD, r, LR) for r in range(WORLD)]
     orcs = [oracle.FsdpShardOracle(shapes, WORLD, r, LR) for r in range(WORLD)]
+    # state bytes count this rank's rows only (not the line padding between
+    # pieces), and over all ranks they cover every parameter once
+    held = [st.state_bytes() for st in states]
+    assert held == [12 * sum(st.local_numel(k) for k in range(len(shapes))) for st in states]
+    assert sum(held) == 12 * sum(int(np.prod(s)) for s in shapes)
     for st, o in zip(states, orcs):
         st.load_master([p.detach() for p in params])
         o.load_master([bits(p.detach()).reshape(-1) for p in params])

@@ -55,6 +55,7 @@ def lib():
     L.zero_shard_geometry.argtypes = [i64, i32, i32, p64, p64, p64]
     L.zero_shard_init.argtypes = [i64, i32, i32, dbl, dbl, dbl, dbl, ctypes.POINTER(vp)]
     L.zero_shard_info.argtypes = [vp, p64, p64, p64]
+    L.zero_shard_state_bytes.argtypes = [vp, p64]
     L.zero_set_lr.argtypes = [vp, dbl]
     L.zero_load_master.argtypes = [vp, vp, ctypes.c_int, i64, vp]
     L.zero_flatten.argtypes = [vp, vp, vp, i32, ctypes.c_int, vp, vp]
@@ -183,6 +184,12 @@ class ShardState:
         """Cap later flat-layout steps at per_cu workgroups per compute unit
         (0: uncapped); results are unchanged."""
         _check(lib().zero_set_step_workgroups(self._h, int(per_cu)))
+
+    def state_bytes(self) -> int:
+        """Bytes of fp32 master, m and v this rank holds (12 per element)."""
+        out = ctypes.c_int64()
+        _check(lib().zero_shard_state_bytes(self._h, ctypes.byref(out)))
+        return out.value
 
     def set_lr(self, lr: float):
         _check(lib().zero_set_lr(self._h, float(lr)))

@@ -628,6 +628,17 @@ int zero_shard_info(const zero_ctx *c, int64_t *shard, int64_t *lo, int64_t *pad
     return ZERO_OK;
 }
 
+int zero_shard_state_bytes(const zero_ctx *c, int64_t *bytes) {
+    if (!c || !bytes) return fail(ZERO_EINVAL, "null context or output pointer");
+    int64_t elems = c->shard;
+    if (c->fsdp) {
+        elems = 0;
+        for (const zero_fsdp_tensor &t : c->tensors) elems += t.rows * t.row_numel;
+    }
+    *bytes = 3 * (int64_t)sizeof(float) * elems;
+    return ZERO_OK;
+}
+
 int zero_set_lr(zero_ctx *c, double lr) {
     if (!c) return fail(ZERO_EINVAL, "null context");
     if (!std::isfinite(lr)) return fail(ZERO_EINVAL, "lr must be finite");
