@@ -142,3 +142,34 @@ def test_zero_row_parameters():
     shapes = [(0,), (9, 4), (0, 5), (3,), (130, 2)]
     for rank in range(4):
         _run(shapes, 4, rank, torch.bfloat16, torch.bfloat16, 2)
+
+
+def _random_shapes(rng):
+    shapes = []
+    for _ in range(int(rng.choice([1, 5, 33, 70]))):
+        kind = rng.random()
+        if kind < 0.1:
+            shapes.append((0,) if rng.random() < 0.5 else (0, int(rng.integers(1, 9))))
+        elif kind < 0.5:
+            shapes.append((int(rng.integers(1, 5000)),))
+        elif kind < 0.9:
+            shapes.append((int(rng.integers(1, 300)), int(rng.integers(1, 300))))
+        else:
+            shapes.append((int(rng.integers(1, 40)), int(rng.integers(1, 9)), int(rng.integers(1, 70))))
+    return shapes
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_parameter_lists(case):
+    """Seeded random parameter lists (zero-row, 1-D, 2-D and 3-D shapes; up
+    to 70 parameters, so several launches of 32 or 16), world and rank
+    (ranks that hold no rows of some parameters), both dtypes: 3 steps,
+    bit-exact against the per-parameter oracle."""
+    rng = np.random.default_rng(50_000 + case)
+    world = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 13, 16]))
+    rank = int(rng.integers(0, world))
+    gdt = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    odt = torch.bfloat16 if rng.random() < 0.7 else torch.float32
+    shapes = _random_shapes(rng)
+    log(f"fsdp case {case}: {len(shapes)} parameters, N={world} r{rank} {gdt}->{odt}")
+    _run(shapes, world, rank, gdt, odt, 3, seed=case)
