@@ -186,8 +186,12 @@ int zero_step(zero_ctx *ctx, const void *const *grad_replicas,
  * param_out[param_offset + i], for i < count, with the same arithmetic, so
  * covering the shard with disjoint ranges gives results bit-identical to
  * one zero_step. Ranges launched on different streams must be disjoint;
- * the library does not order them. Any range start takes the vector path
- * after a head of at most 63 elements.
+ * the library does not order them. Neighbouring ranges running at once
+ * write different elements of the same cache lines (state and output), so
+ * param_out must be ordinary device memory (hipMalloc, torch): an output
+ * from hipExtMallocWithFlags(..., hipDeviceMallocContiguous) was seen to
+ * lose such writes when the library's own state lived there. Any range
+ * start takes the vector path after a head of at most 63 elements.
  * EINVAL: as zero_step, plus shard_begin < 0, count < 0 or
  * shard_begin + count > shard. count == 0 is a no-op. */
 int zero_step_range(zero_ctx *ctx, int64_t shard_begin, int64_t count,
