@@ -47,12 +47,21 @@ constexpr int kGroup = 8;            // replicas loaded together
 //
 // Dynamic LDS reserved (unused) per fused-step workgroup: caps how many
 // workgroups share a CU (160 KiB of LDS per CU). The default keeps six
-// one-wave workgroups per CU: measured best (79.0% of peak HBM bandwidth
-// against 77.9% at seven, 77.3% at eight and 75.4% at ten on the 7e9/N=8
+// one-wave workgroups per CU: measured best (with the block's buffer
+// instructions 80.2% of peak HBM bandwidth against 79.1% at eight, 78.8% at
+// seven and 72.3% at five; earlier with flat global instructions 79.0%
+// against 77.9% at seven, 77.3% at eight and 75.4% at ten, on the 7e9/N=8
 // shard), since more waves put more of the step's 12 streams' requests in
 // flight than the HBM serves well, and fewer leave it idle.
 #ifndef ZK_STEP_LDS
 #define ZK_STEP_LDS 26624
+#endif
+// Sixteen replicas put twice the loads of eight in flight per wave (the
+// block's pinned load order, below): four workgroups per CU gave 77.6% of
+// peak against 77.1% at five, 74.0% at six and 71.3% at three (7e9/N=16
+// shard; the earlier global-load kernel at six: 77.4%).
+#ifndef ZK_STEP_LDS_WIDE
+#define ZK_STEP_LDS_WIDE 40960
 #endif
 // The same for the shifted path, which does more per lane (cross-lane
 // realignment, the last lane's own loads, narrow stores) and measured best
@@ -90,6 +99,42 @@ constexpr int kGroup = 8;            // replicas loaded together
 #endif
 #ifndef ZK_NT_COPY
 #define ZK_NT_COPY 1
+#endif
+// Cache-policy bits of the buffer instructions of a full wavefront block of
+// the fused step (gfx950 encoding: sc0 = 1, nt = 2, sc1 = 16). Streamed
+// state and the output are stored non-temporal at device scope (nt sc1):
+// 80.2-80.7% of peak HBM bandwidth on the 7e9/N=8 shard against 79.5-79.6%
+// with nt alone and 79.0% for the same access pattern through flat global
+// instructions (interleaved in one process, three runs). Device scope on
+// the state stores alone gave 80.3%, on the output alone 77.9%; sc0 nt sc1
+// 80.3%, sc0 nt 79.7%, sc1 alone 79.0%; the same bits on the loads
+// (nt sc1, sc0 nt) 79.1-79.2%, and default-policy loads of the replicas or
+// of the state 79.3-79.4%. Global loads with these buffer stores gave
+// 78.8%: the gain needs the buffer loads as well.
+#ifndef ZK_POL_STORE_STREAM
+#define ZK_POL_STORE_STREAM 18
+#endif
+// State that stays in the Infinity Cache between steps (12 S bytes within
+// its 256 MB) is loaded and stored at device scope without the streaming
+// hint (sc1): 83.8% of peak on the GPT-2-small shard (N = 8, rank 3)
+// against 79.0% with default-policy loads and 83.2% with both default; sc1
+// stores with default loads 87.0% / 79.0% in two runs, sc0 sc1 stores
+// 78.9%, nt sc1 stores 72.6-78.4%, nt stores 77.8-81.6%, sc0 loads 80.1%.
+// Its output keeps the plain non-temporal hint (nt sc1 or no hint: within
+// 0.3 points).
+#ifndef ZK_POL_STORE_CACHED
+#define ZK_POL_STORE_CACHED 16
+#endif
+#ifndef ZK_POL_LOAD_CACHED
+#define ZK_POL_LOAD_CACHED 16
+#endif
+#ifndef ZK_POL_OUT_CACHED
+#define ZK_POL_OUT_CACHED 2
+#endif
+// Replica counts up to this take the pinned load order of a block (the
+// replicas, m and v in one round trip, then master).
+#ifndef ZK_PIN_MAX
+#define ZK_PIN_MAX 16
 #endif
 // Master initialisation: dynamic LDS reserved (unused) per one-wave
 // workgroup, six per compute unit as for the fused step. Its three write
@@ -156,6 +201,45 @@ __device__ __forceinline__ void st_f4(void *p, float4 v) {
     }
 }
 
+// Buffer instructions over one wave-uniform span: the descriptor (base in
+// scalar registers, byte addressing, range = the span) is built per span,
+// and each lane passes a 32-bit byte offset into it. An access past the
+// span reads zero and writes nothing. Word 3 is the gfx9 family's raw
+// (untyped) buffer format.
+constexpr int kPolDefault = 0;
+constexpr int kPolNT = 2;
+typedef __amdgpu_buffer_rsrc_t span_t;
+
+__device__ __forceinline__ span_t span_of(const void *base, int nbytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, nbytes,
+                                             0x00020000);
+}
+
+template <int POL>
+__device__ __forceinline__ uint2 bld_u2(span_t r, int off) {
+    u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, POL);
+    return make_uint2(v.x, v.y);
+}
+
+template <int POL>
+__device__ __forceinline__ float4 bld_f4(span_t r, int off) {
+    u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POL);
+    return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                       __uint_as_float(v.w));
+}
+
+template <int POL>
+__device__ __forceinline__ void bst_u2(span_t r, int off, uint2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{v.x, v.y}, r, off, 0, POL);
+}
+
+template <int POL>
+__device__ __forceinline__ void bst_f4(span_t r, int off, float4 v) {
+    u32x4_t w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                 __float_as_uint(v.w)};
+    __builtin_amdgcn_raw_buffer_store_b128(w, r, off, 0, POL);
+}
+
 __device__ __forceinline__ float widen_bf16(uint32_t bits16) {
     return __uint_as_float(bits16 << 16);
 }
@@ -168,17 +252,24 @@ __device__ __forceinline__ uint32_t round_bf16(float x) {
     return ((u & 0x7FFFFFFFu) > 0x7F800000u) ? ((u >> 16) | 0x40u) : r;
 }
 
-// One element of the Adam update; p/m/v updated in place.
-__device__ __forceinline__ void adam_update(float g, float &p, float &m,
-                                            float &v, const StepScalars &sc) {
+// One element of the Adam update in two parts: the moments (m, v updated in
+// place) give the step u, which the parameter then takes (p - u).
+__device__ __forceinline__ float adam_moments(float g, float &m, float &v,
+                                              const StepScalars &sc) {
     float mm = __builtin_fmaf(g, sc.c1, m * sc.b1);
     float vv = __builtin_fmaf(sc.c2 * g, g, v * sc.b2);
     float mh = mm / sc.bc1;
     float vh = vv / sc.bc2;
     float den = __builtin_sqrtf(vh) + sc.eps;
-    float u = (sc.lr * mh) / den;
     m = mm;
     v = vv;
+    return (sc.lr * mh) / den;
+}
+
+// One element of the Adam update; p/m/v updated in place.
+__device__ __forceinline__ void adam_update(float g, float &p, float &m,
+                                            float &v, const StepScalars &sc) {
+    const float u = adam_moments(g, m, v, sc);
     p = p - u;
 }
 
@@ -331,20 +422,22 @@ template <bool GB> struct SplitRaw;
 template <> struct SplitRaw<true> { uint2 a, b; };
 template <> struct SplitRaw<false> { float4 a, b; };
 
-// NTG: non-temporal hints on the replica loads (see StepArgs::nt_grad).
-template <bool GB, bool NTG>
-__device__ __forceinline__ SplitRaw<GB> load_split(const void *base, int64_t q0) {
-    SplitRaw<GB> r;
+// Bytes of one full wavefront block of a stream of the given element size.
+template <int ES> constexpr int kSpanBytes = kBlock * kVec * ES;
+
+// A lane's two quads of one replica's block (GPOL: its cache policy).
+template <bool GB, int GPOL>
+__device__ __forceinline__ SplitRaw<GB> load_split(span_t r) {
+    const int l = threadIdx.x;
+    SplitRaw<GB> x;
     if constexpr (GB) {
-        const uint2 *p = reinterpret_cast<const uint2 *>(base);
-        r.a = ld_u2<NTG>(p + q0);
-        r.b = ld_u2<NTG>(p + q0 + kBlock);
+        x.a = bld_u2<GPOL>(r, 8 * l);
+        x.b = bld_u2<GPOL>(r, 8 * (kBlock + l));
     } else {
-        const float4 *p = reinterpret_cast<const float4 *>(base);
-        r.a = ld_f4<NTG>(p + q0);
-        r.b = ld_f4<NTG>(p + q0 + kBlock);
+        x.a = bld_f4<GPOL>(r, 16 * l);
+        x.b = bld_f4<GPOL>(r, 16 * (kBlock + l));
     }
-    return r;
+    return x;
 }
 
 __device__ __forceinline__ void unpack(const SplitRaw<true> &r, float (&x)[kVec]) {
@@ -359,28 +452,33 @@ __device__ __forceinline__ void unpack(const SplitRaw<false> &r, float (&x)[kVec
     x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
 }
 
-template <bool NT>
-__device__ __forceinline__ void load8_split(const float *base, int64_t q0, float (&x)[kVec]) {
-    const float4 *p = reinterpret_cast<const float4 *>(base);
-    float4 a = ld_f4<NT>(p + q0), b = ld_f4<NT>(p + q0 + kBlock);
+template <int POL>
+__device__ __forceinline__ void load8_split(span_t r, float (&x)[kVec]) {
+    const int l = threadIdx.x;
+    float4 a = bld_f4<POL>(r, 16 * l), b = bld_f4<POL>(r, 16 * (kBlock + l));
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
     x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-template <bool NT>
-__device__ __forceinline__ void store8_split(float *base, int64_t q0, const float (&x)[kVec]) {
-    float4 *p = reinterpret_cast<float4 *>(base);
-    st_f4<NT>(p + q0, make_float4(x[0], x[1], x[2], x[3]));
-    st_f4<NT>(p + q0 + kBlock, make_float4(x[4], x[5], x[6], x[7]));
+template <int POL>
+__device__ __forceinline__ void store8_split(span_t r, const float (&x)[kVec]) {
+    const int l = threadIdx.x;
+    bst_f4<POL>(r, 16 * l, make_float4(x[0], x[1], x[2], x[3]));
+    bst_f4<POL>(r, 16 * (kBlock + l), make_float4(x[4], x[5], x[6], x[7]));
 }
 
-template <int NR, bool GB, bool NTG>
+// Fold replicas q0r .. q0r + kGroup - 1 of block blk into s (rank order).
+// The group's loads are all issued before the first add consumes them.
+template <int NR, bool GB, int GPOL>
 __device__ __forceinline__ void fold_group_split(const Reps<NR> &reps, int q0r, int n,
-                                                 int64_t q0, float (&s)[kVec]) {
+                                                 int64_t blk, float (&s)[kVec]) {
+    constexpr int gbytes = kSpanBytes<GB ? 2 : 4>;
     SplitRaw<GB> raw[kGroup];
 #pragma unroll
     for (int k = 0; k < kGroup; ++k)
-        if (q0r + k < n) raw[k] = load_split<GB, NTG>(reps.p[q0r + k], q0);
+        if (q0r + k < n)
+            raw[k] = load_split<GB, GPOL>(
+                span_of(static_cast<const char *>(reps.p[q0r + k]) + blk * gbytes, gbytes));
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) {
         if (q0r + k < n) {
@@ -397,62 +495,110 @@ __device__ __forceinline__ void fold_group_split(const Reps<NR> &reps, int q0r, 
     }
 }
 
-// The fused step on quads q0 and q0 + kBlock (split lane layout); NTS:
-// non-temporal hints on the master/m/v loads and stores, NTG on the
-// replica loads.
+// The fused step on full wavefront block blk (elements blk * 8 * kBlock
+// onwards of every stream, which lie on 16-byte boundaries) in the split
+// lane layout, through buffer instructions over each stream's block.
+// NTS: master/m/v streamed (non-temporal loads, stores at the streaming
+// policy) rather than kept in the Infinity Cache; NTG: non-temporal replica
+// loads.
 template <int NR, bool GB, bool PB, bool NTS, bool NTG>
-__device__ __forceinline__ void step_vector_split(const Reps<NR> &reps, int n, bool pow2,
-                                                  float *__restrict__ master,
-                                                  float *__restrict__ mom,
-                                                  float *__restrict__ var, void *__restrict__ out,
-                                                  int64_t q0, const StepScalars &sc) {
-    // Replicas first, then the state: measured 0.3-1% faster than the
-    // reverse order (issuing every load before the first wait, pinned with a
-    // scheduling barrier, measured 6% slower than either).
-    float s[kVec];
-    if constexpr (NR > 0 && NR <= 2 * kGroup) {
+__device__ __forceinline__ void step_block_split(const Reps<NR> &reps, int n, bool pow2,
+                                                 float *master, float *mom, float *var, void *out,
+                                                 int64_t blk, const StepScalars &sc) {
+    constexpr int kGPol = NTG ? kPolNT : kPolDefault;
+    constexpr int kSLoad = NTS ? kPolNT : ZK_POL_LOAD_CACHED;
+    constexpr int kSStore = NTS ? ZK_POL_STORE_STREAM : ZK_POL_STORE_CACHED;
+    constexpr int kOStore = !ZK_NT_OUT ? kPolDefault
+                                       : (NTS ? ZK_POL_STORE_STREAM : ZK_POL_OUT_CACHED);
+    constexpr int sbytes = kSpanBytes<4>;
+    constexpr int obytes = kSpanBytes<PB ? 2 : 4>;
+    constexpr int gbytes = kSpanBytes<GB ? 2 : 4>;
+    const int64_t so = blk * (kBlock * kVec);
+    const span_t rp = span_of(master + so, sbytes), rm = span_of(mom + so, sbytes),
+                 rv = span_of(var + so, sbytes);
+    float s[kVec], p[kVec], m[kVec], v[kVec], g[kVec];
+    if constexpr (NR > 0 && NR <= ZK_PIN_MAX) {
+        // Up to ZK_PIN_MAX replicas: the replicas, m and v in one round
+        // trip, and master, whose value is needed last, loaded once the
+        // moments are done; scheduling barriers keep that order. Measured
+        // 80.3% of peak HBM bandwidth against 79.2% with every load in one
+        // round trip (7e9/N=8 shard, interleaved in one process).
+        // NR is a capacity where the count comes at run time (n <= NR): only
+        // the first n table entries are replicas
+        SplitRaw<GB> raw[NR];
 #pragma unroll
-        for (int r = 0; r < NR; r += kGroup) fold_group_split<NR, GB, NTG>(reps, r, n, q0, s);
+        for (int k = 0; k < NR; ++k)
+            if (k < n)
+                raw[k] = load_split<GB, kGPol>(
+                    span_of(static_cast<const char *>(reps.p[k]) + blk * gbytes, gbytes));
+        load8_split<kSLoad>(rm, m);
+        load8_split<kSLoad>(rv, v);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            if (k < n) {
+                float x[kVec];
+                unpack(raw[k], x);
+#pragma unroll
+                for (int e = 0; e < kVec; ++e) s[e] = k == 0 ? x[e] : s[e] + x[e];
+            }
+        }
+        if (pow2) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
+        }
+        float u[kVec];
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) u[e] = adam_moments(g[e], m[e], v[e], sc);
+        __builtin_amdgcn_sched_barrier(0);
+        load8_split<kSLoad>(rp, p);
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) p[e] = p[e] - u[e];
     } else {
+        // Replicas first, then the state: measured 0.3-1% faster than the
+        // reverse order (issuing every load before the first wait, pinned
+        // with a scheduling barrier, measured 6% slower than either).
+        if constexpr (NR > 0 && NR <= 2 * kGroup) {
+#pragma unroll
+            for (int r = 0; r < NR; r += kGroup)
+                fold_group_split<NR, GB, kGPol>(reps, r, n, blk, s);
+        } else {
 #pragma unroll 1
-        for (int r = 0; r < n; r += kGroup) fold_group_split<NR, GB, NTG>(reps, r, n, q0, s);
+            for (int r = 0; r < n; r += kGroup)
+                fold_group_split<NR, GB, kGPol>(reps, r, n, blk, s);
+        }
+        load8_split<kSLoad>(rp, p);
+        load8_split<kSLoad>(rm, m);
+        load8_split<kSLoad>(rv, v);
+        if (pow2) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;
+        } else {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
+        }
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
     }
-    float p[kVec], m[kVec], v[kVec];
-    load8_split<NTS>(master, q0, p);
-    load8_split<NTS>(mom, q0, m);
-    load8_split<NTS>(var, q0, v);
 
-    float g[kVec];
-    if (pow2) {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;
-    } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
-    }
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
-
-    store8_split<NTS>(master, q0, p);
-    store8_split<NTS>(mom, q0, m);
-    store8_split<NTS>(var, q0, v);
-    if (PB) {
+    store8_split<kSStore>(rp, p);
+    store8_split<kSStore>(rm, m);
+    store8_split<kSStore>(rv, v);
+    const span_t ro = span_of(static_cast<char *>(out) + blk * obytes, obytes);
+    if constexpr (PB) {
         uint2 a, b;
         a.x = round_bf16(p[0]) | (round_bf16(p[1]) << 16);
         a.y = round_bf16(p[2]) | (round_bf16(p[3]) << 16);
         b.x = round_bf16(p[4]) | (round_bf16(p[5]) << 16);
         b.y = round_bf16(p[6]) | (round_bf16(p[7]) << 16);
-        uint2 *o = reinterpret_cast<uint2 *>(out);
-        if (ZK_NT_OUT) {
-            __builtin_nontemporal_store(u32x2_t{a.x, a.y}, reinterpret_cast<u32x2_t *>(o + q0));
-            __builtin_nontemporal_store(u32x2_t{b.x, b.y},
-                                        reinterpret_cast<u32x2_t *>(o + q0 + kBlock));
-        } else {
-            o[q0] = a;
-            o[q0 + kBlock] = b;
-        }
+        const int l = threadIdx.x;
+        bst_u2<kOStore>(ro, 8 * l, a);
+        bst_u2<kOStore>(ro, 8 * (kBlock + l), b);
     } else {
-        store8_split<ZK_NT_OUT>(reinterpret_cast<float *>(out), q0, p);
+        store8_split<kOStore>(ro, p);
     }
 }
 
@@ -492,14 +638,17 @@ step_vec_kernel(Reps<NR> reps, int nrep, float *__restrict__ master,
     const int64_t nfull = nvec / kBlock;
     const int64_t w = blockIdx.x;
     if (w < nbw) {
-        for (int64_t blk = w; blk < nfull; blk += nbw) {
-            const int64_t q0 = blk * 2 * kBlock + threadIdx.x;
-            if (nt_state)
-                step_vector_split<NR, GB, PB, true, NTG>(reps, n, pow2, master, mom, var, out, q0,
-                                                         sc);
-            else
-                step_vector_split<NR, GB, PB, false, NTG>(reps, n, pow2, master, mom, var, out,
-                                                          q0, sc);
+        // one loop per state policy: with the branch inside the loop body the
+        // compiler hoists the replica loads, common to both, above it, and
+        // the state loads can no longer share their round trip
+        if (nt_state) {
+            for (int64_t blk = w; blk < nfull; blk += nbw)
+                step_block_split<NR, GB, PB, true, NTG>(reps, n, pow2, master, mom, var, out, blk,
+                                                        sc);
+        } else {
+            for (int64_t blk = w; blk < nfull; blk += nbw)
+                step_block_split<NR, GB, PB, false, NTG>(reps, n, pow2, master, mom, var, out,
+                                                         blk, sc);
         }
         return;
     }
@@ -929,7 +1078,13 @@ __device__ __forceinline__ void step_block_split_shift(const ShiftReps<NR> &reps
                                                        int64_t blk, const StepScalars &sc) {
     const int64_t q0 = blk * 2 * kBlock + threadIdx.x;    // state quad of half 0
     const int64_t ub = blk * 2 * kBlock + threadIdx.x;    // replica unit of half 0 at d = 0
-    float s[kVec];
+    constexpr int kSLoad = NTS ? kPolNT : ZK_POL_LOAD_CACHED;
+    constexpr int kSStore = NTS ? ZK_POL_STORE_STREAM : ZK_POL_STORE_CACHED;
+    constexpr int sbytes = kSpanBytes<4>;
+    const int64_t so = blk * (kBlock * kVec);
+    const span_t rp = span_of(master + so, sbytes), rm = span_of(mom + so, sbytes),
+                 rv = span_of(var + so, sbytes);
+    float s[kVec], p[kVec], m[kVec], v[kVec], g[kVec];
     if constexpr (NR > 0 && NR <= 2 * kGroup) {
 #pragma unroll
         for (int r = 0; r < NR; r += kGroup) fold_group_split_shift<NR, GB>(reps, r, n, ub, s);
@@ -937,11 +1092,13 @@ __device__ __forceinline__ void step_block_split_shift(const ShiftReps<NR> &reps
 #pragma unroll 1
         for (int r = 0; r < n; r += kGroup) fold_group_split_shift<NR, GB>(reps, r, n, ub, s);
     }
-    float p[kVec], m[kVec], v[kVec];
-    load8_split<NTS>(master, q0, p);
-    load8_split<NTS>(mom, q0, m);
-    load8_split<NTS>(var, q0, v);
-    float g[kVec];
+    // m and v, then master once the moments are done. Issuing m and v before
+    // the replica work, or all three state loads after it, or flat global
+    // state accesses measured within a point of this either way (7e9/N=8
+    // shard, 7 replicas one element off and 1 replica with the output 3 off,
+    // three states per variant interleaved in one process).
+    load8_split<kSLoad>(rm, m);
+    load8_split<kSLoad>(rv, v);
     if (pow2) {
 #pragma unroll
         for (int e = 0; e < kVec; ++e) g[e] = s[e] * sc.inv_n;
@@ -949,11 +1106,15 @@ __device__ __forceinline__ void step_block_split_shift(const ShiftReps<NR> &reps
 #pragma unroll
         for (int e = 0; e < kVec; ++e) g[e] = s[e] / sc.nf;
     }
+    float u[kVec];
 #pragma unroll
-    for (int e = 0; e < kVec; ++e) adam_update(g[e], p[e], m[e], v[e], sc);
-    store8_split<NTS>(master, q0, p);
-    store8_split<NTS>(mom, q0, m);
-    store8_split<NTS>(var, q0, v);
+    for (int e = 0; e < kVec; ++e) u[e] = adam_moments(g[e], m[e], v[e], sc);
+    load8_split<kSLoad>(rp, p);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) p[e] = p[e] - u[e];
+    store8_split<kSStore>(rp, p);
+    store8_split<kSStore>(rm, m);
+    store8_split<kSStore>(rv, v);
     const int64_t e0 = 4 * q0, e1 = 4 * (q0 + kBlock);    // first element of each quad
     if (PB) {
         uint16_t *o = reinterpret_cast<uint16_t *>(out);
@@ -985,11 +1146,12 @@ step_shift_kernel(ShiftReps<NR> reps, int nrep, float *__restrict__ master,
     const int64_t nfull = nvec / kBlock;
     const int64_t w = blockIdx.x;
     if (w < nbw) {                                   // full blocks, as step_vec_kernel
-        for (int64_t blk = w; blk < nfull; blk += nbw) {
-            if (nt_state)
+        if (nt_state) {
+            for (int64_t blk = w; blk < nfull; blk += nbw)
                 step_block_split_shift<NR, GB, PB, true>(reps, n, pow2, master, mom, var, out,
                                                          dout, blk, sc);
-            else
+        } else {
+            for (int64_t blk = w; blk < nfull; blk += nbw)
                 step_block_split_shift<NR, GB, PB, false>(reps, n, pow2, master, mom, var, out,
                                                           dout, blk, sc);
         }
@@ -1098,13 +1260,12 @@ fsdp_step_kernel(FsdpBatch<NR> b, int nrep, float *__restrict__ master,
     for (int q = 0; q < n; ++q) aligned = aligned && ((uintptr_t)reps.p[q] % 16) == 0;
     const int64_t chunk = w - b.blk0[sgi];
     if (aligned && (chunk + 1) * kBlock * kVec <= numel) {
-        const int64_t q0 = chunk * 2 * kBlock + threadIdx.x;
         if (nt_state)
-            step_vector_split<NR, GB, PB, true, ZK_NT_GRAD>(reps, n, pow2, ms, mm, vs, out, q0,
-                                                            sc);
+            step_block_split<NR, GB, PB, true, ZK_NT_GRAD>(reps, n, pow2, ms, mm, vs, out, chunk,
+                                                           sc);
         else
-            step_vector_split<NR, GB, PB, false, ZK_NT_GRAD>(reps, n, pow2, ms, mm, vs, out, q0,
-                                                             sc);
+            step_block_split<NR, GB, PB, false, ZK_NT_GRAD>(reps, n, pow2, ms, mm, vs, out, chunk,
+                                                            sc);
         return;
     }
     const int64_t j = chunk * kBlock + threadIdx.x;     // vector index
@@ -1133,7 +1294,7 @@ hipError_t launch_fsdp_typed(const FsdpArgs &a, hipStream_t stream) {
     const int64_t per_block = (int64_t)kBlock * kVec;
     int i = 0;
     while (i < a.nseg) {
-        FsdpBatch<NR> b;
+        FsdpBatch<NR> b = {};
         b.nseg = 0;
         int64_t blocks = 0;
         while (i < a.nseg && b.nseg < FsdpBatch<NR>::kMax) {
@@ -1187,7 +1348,7 @@ inline unsigned occupancy_lds(const StepArgs &a, unsigned lds) {
 template <int NR, bool GB, bool PB, bool DS>
 hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail,
                       hipStream_t stream) {
-    Reps<NR> reps;
+    Reps<NR> reps = {};
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
     const int64_t nfull = nvec / kBlock, nbw = block_workgroups(a, nfull);
     const int64_t grid = nbw + (nfull * kBlock < nvec ? 1 : 0) + (head + tail > 0 ? 1 : 0);
@@ -1196,7 +1357,8 @@ hipError_t launch_vec(const StepArgs &a, int64_t nvec, int head, int tail,
     // replica cache policy as a template parameter: a runtime choice inside
     // the kernel measured 2 points slower on line-aligned streams
     const dim3 g((unsigned)grid), b(kBlock);
-    const unsigned lds = occupancy_lds(a, ZK_STEP_LDS);
+    constexpr unsigned kLds = (NR > kGroup && NR <= 2 * kGroup) ? ZK_STEP_LDS_WIDE : ZK_STEP_LDS;
+    const unsigned lds = occupancy_lds(a, kLds);
     const int nts = a.stream_state ? 1 : 0;
     if (a.nt_grad)
         hipLaunchKernelGGL((step_vec_kernel<NR, GB, PB, DS, true>), g, b, lds, stream, reps, a.n,
@@ -1225,7 +1387,7 @@ hipError_t dispatch_vec(const StepArgs &a, int64_t nvec, int head, int tail,
 
 template <bool GB, bool PB, bool DS>
 hipError_t launch_elem(const StepArgs &a, int64_t begin, int64_t end, hipStream_t stream) {
-    Reps<0> reps;
+    Reps<0> reps = {};
     for (int q = 0; q < a.n; ++q) reps.p[q] = a.grads[q];
     int64_t want = (end - begin + kElemBlock - 1) / kElemBlock;
     int64_t cap = (int64_t)a.num_cus * 8;
@@ -1305,7 +1467,7 @@ inline int shifted_head(const StepArgs &a) {
 template <int NR, bool GB, bool PB, bool DS>
 hipError_t launch_shift(const StepArgs &a, int h, int64_t nvec, int tail, hipStream_t stream) {
     const int ge = a.grad_bf16 ? 2 : 4, oe = a.out_bf16 ? 2 : 4;
-    ShiftReps<NR> reps;
+    ShiftReps<NR> reps = {};
     for (int q = 0; q < a.n; ++q) {
         const uintptr_t e0 = (uintptr_t)a.grads[q] + (uintptr_t)ge * h;
         reps.d[q] = (uint8_t)((e0 % 16) / ge);
