@@ -38,10 +38,10 @@
  *     lo mod 32 fp32, elements past a line) keeps every stream on whole
  *     lines. Buffers at other 16-byte phases take a shifted path: on the
  *     7e9-element shard at N = 8, seven replicas one element off ran at
- *     77.5% of 8 TB/s and an output one element off at 75.4%, against about
- *     79% with every stream on its lines. Buffers whose slices start on
- *     4 KiB pages run fastest (each replica 512 bytes off its page costs
- *     about 0.4% of the step).
+ *     about 78% of 8 TB/s and one replica with the output three off at
+ *     about 75%, against 80-81% with every stream on its lines. Buffers
+ *     whose slices start on 4 KiB pages run fastest (each replica 512 bytes
+ *     off its page costs about 0.4% of the step).
  *   - The library owns the context and its master/m/v buffers; the caller
  *     owns every pointer it passes, and its streams.
  *   - Output buffers must not overlap any input of the same call (the
