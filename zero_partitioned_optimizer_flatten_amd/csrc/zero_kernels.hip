@@ -65,12 +65,16 @@ constexpr int kGroup = 8;            // replicas loaded together
 #endif
 // The same for the shifted path, which does more per lane (cross-lane
 // realignment, the last lane's own loads, narrow stores) and measured best
-// with more waves: twelve per CU gave 77.8% / 77.6% of peak HBM bandwidth
-// against 76.9% / 74.6% at ten, 74.6% / 75.9% at fourteen and 72.9% / 73.9%
-// at sixteen (7e9-element shard, N = 8; seven replicas one element off the
-// state's phase / one replica and the output three off).
+// with more waves. With its state behind the block's buffer instructions,
+// ten per CU gave 77.0-77.4% of peak HBM bandwidth against 72.0-72.9% at
+// twelve and 75.9-76.3% at eleven on the Llama-13B rank-7 mixed layout,
+// 75.1-76.3% against 72.5-75.3% with one replica and the output three
+// elements off, and 76.5% against 76.2-77.2% (eleven: 78.4-78.9%) with
+// seven replicas one element off (7e9-element shard, N = 8; three states
+// per variant, interleaved in one process). Earlier, with flat global state
+// accesses, twelve had led ten by 0.9-3.0 points on the last two layouts.
 #ifndef ZK_SHIFT_LDS
-#define ZK_SHIFT_LDS 13312
+#define ZK_SHIFT_LDS 16384
 #endif
 // The same for the per-parameter step, whose workgroups first search the
 // segment table (dependent scalar loads) before their first vector load:
