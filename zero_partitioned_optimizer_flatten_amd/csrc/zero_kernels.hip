@@ -22,6 +22,10 @@
 // (about 0.5 flop per byte), so the kernels are written for streaming:
 // 16-byte loads and stores, coalesced across each 64-lane wavefront, with
 // every replica's load for a vector issued before the fold consumes it.
+// Full blocks of the fused step read and write through buffer instructions
+// on per-block descriptors, which carry the whole cache-policy field
+// (device-scope streaming stores), where HIP's flat global instructions
+// only carry the non-temporal hint.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
