@@ -4,9 +4,11 @@ properties the design relies on:
 - no packed fp32 arithmetic (v_pk_add/mul/fma_f32), which the build turns
   off;
 - no kernel uses scratch (no register spills);
-- the fused and per-parameter step kernels carry no readfirstlane loop:
-  every buffer descriptor they build is wave-uniform, so no load or store is
-  wrapped in a loop over the distinct descriptors of a wave;
+- the fused and per-parameter step kernels and the segment copy carry no
+  readfirstlane loop: every buffer descriptor they build is wave-uniform, so
+  no load or store is wrapped in a loop over the distinct descriptors of a
+  wave;
+- the segment copy stores its 16-byte vectors non-temporal at device scope;
 - the streamed-state N = 8 bf16 step stores master/m/v and the parameter
   output non-temporal at device scope (nt sc1), and loads the state and the
   line-aligned replicas non-temporal."""
@@ -49,10 +51,19 @@ def test_no_scratch(asm):
 def test_step_kernels_have_no_waterfall_loops(asm):
     found = 0
     for name, body, _ in _kernels(asm):
-        if "step_vec_kernel" in name or "fsdp_step_kernel" in name:
+        if ("step_vec_kernel" in name or "fsdp_step_kernel" in name
+                or "copy_segments_kernel" in name):
             found += 1
             assert "v_readfirstlane" not in body, name
     assert found >= 100
+
+
+def test_copy_store_policy(asm):
+    bodies = [b for n, b, _ in _kernels(asm) if "copy_segments_kernel" in n]
+    assert len(bodies) == 2                      # both destination chunk grids
+    for body in bodies:
+        stores = re.findall(r"buffer_store_dwordx4 [^\n]*offen([^\n]*)", body)
+        assert stores and all(t.split() == ["nt", "sc1"] for t in stores), stores
 
 
 def test_streamed_step_cache_policy(asm):
